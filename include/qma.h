@@ -1,0 +1,323 @@
+/*
+ * qma.h -- C ABI of libqma, an MI355X (gfx950) library for the W4A16 MoE
+ * expert GEMM pair: gate_up, then a gated activation, then down.
+ * Weights are uint4 with group-32 bf16 scales; activations are bf16.
+ *
+ * Sources. The operation is the one described in two pages:
+ *   [release]  "vLLM and Novita AI release Chord: a fast INT4 MoE kernel for
+ *              Kimi K2.x" (agentlenshq.com, Japanese);
+ *   [announce] "vLLM announces that the Humming backend can run Novita's
+ *              open-source Chord kernel" (arex-research.com, Chinese).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers owned by the caller. Tensors are
+ *     contiguous and row-major, and 16-byte aligned unless a call says
+ *     otherwise. The library never frees or retains them past the call.
+ *   - bf16 values are passed as uint16_t bit patterns; indices are int32.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     GPU calls only enqueue work on it. None synchronises with the host
+ *     except qma_validate_routing, and none allocates device memory (a
+ *     workspace is passed in where one is needed). The trusted forward
+ *     path is therefore capturable in a hipGraph ([release] runtime
+ *     considerations: capturable when routing validation is off).
+ *   - Every call returns a qma_status and never aborts. On failure,
+ *     qma_last_error_detail() returns text for the calling thread.
+ *   - Host objects (qma_layer_t, qma_plan_t) are immutable once created
+ *     and may be shared between threads.
+ */
+#ifndef QMA_H
+#define QMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum qma_status {
+  QMA_OK = 0,
+  QMA_ERR_INVALID_ARG = 1,   /* null pointer, bad shape, short capacity */
+  QMA_ERR_UNSUPPORTED = 2,   /* quantisation scheme this library rejects */
+  QMA_ERR_ROUTING = 3,       /* routing buffers fail validation */
+  QMA_ERR_WORKSPACE = 4,     /* workspace missing or too small */
+  QMA_ERR_HIP = 5            /* a HIP runtime call or launch failed */
+} qma_status;
+
+/* The three families of GEMM call ([announce] scheduling section: the
+ * indexed path consumes vLLM's routing tensors; grouped_contiguous
+ * (prefill) and grouped_masked (decode) form a separate family with their
+ * own routing convention). */
+typedef enum qma_path {
+  QMA_PATH_INDEXED = 0,
+  QMA_PATH_GROUPED_CONTIGUOUS = 1,
+  QMA_PATH_GROUPED_MASKED = 2
+} qma_path;
+
+enum { QMA_DTYPE_BF16 = 1, QMA_DTYPE_FP16 = 2, QMA_DTYPE_FP32 = 3 };
+/* 8 uint4 values per int32 word along K; element k % 8 at bits 4*(k%8).. */
+enum { QMA_PACK_INT32_K8 = 1 };
+
+/* Quantisation scheme of a projection ([announce] integration section: the
+ * schema supports uint4, group 32 and BF16 scales; other schemes fail at
+ * load instead of falling back). The only accepted value is
+ * {4, 8, 32, QMA_DTYPE_BF16, QMA_DTYPE_BF16, QMA_PACK_INT32_K8}. */
+typedef struct qma_quant_desc {
+  int32_t weight_bits;   /* 4 */
+  int32_t zero_point;    /* 8: w = (q - 8) * scale */
+  int32_t group_size;    /* 32 elements of K per scale */
+  int32_t scale_dtype;   /* QMA_DTYPE_BF16 */
+  int32_t act_dtype;     /* QMA_DTYPE_BF16 */
+  int32_t pack_format;   /* QMA_PACK_INT32_K8 */
+} qma_quant_desc;
+
+/* Profile inferred from the projection's shape alone, with no shard
+ * arguments ([release] runtime considerations). EP shares hold a few
+ * experts with large N*K each; TP shares hold many experts with N or K cut
+ * by the tensor-parallel degree. */
+typedef enum qma_profile {
+  QMA_PROFILE_GENERIC = 0,
+  QMA_PROFILE_EP_GATE_UP = 1,
+  QMA_PROFILE_EP_DOWN = 2,
+  QMA_PROFILE_TP_GATE_UP = 3,
+  QMA_PROFILE_TP_DOWN = 4
+} qma_profile;
+
+typedef struct qma_layer qma_layer_t;
+
+/* GEMM kernel families the planner chooses between. */
+typedef enum qma_kernel {
+  /* Few rows per expert (decode): dequantised weights occupy the MFMA row
+   * side and tokens the 16-wide column side ([announce] scheduling section:
+   * decode swaps the MMA operands). HBM-bound. */
+  QMA_KERNEL_SMALL_M = 1,
+  /* Many rows per expert (prefill): token tiles staged in LDS, weights
+   * dequantised into the MFMA column side. MFMA-bound. */
+  QMA_KERNEL_LARGE_M = 2
+} qma_kernel;
+
+/* A plan: a pure function of the layer's shape and the host-known token
+ * counts ([announce] scheduling section: the schedule follows the routed
+ * tokens per expert, not the total; profile and layout are fixed at load
+ * and the token count only tunes the schedule within them). Every field is
+ * plain data so tests can check the rules. */
+typedef struct qma_plan {
+  int32_t path;          /* qma_path of the layer */
+  int32_t kernel;        /* qma_kernel */
+  int32_t block_m;       /* rows per routing block (the moe_align block size) */
+  int32_t block_n;       /* output columns per workgroup */
+  int32_t split_k;       /* K partitions across workgroups; 1 = off */
+  int32_t k_depth;       /* K elements in flight per wave */
+  int32_t num_experts;   /* E of the layer */
+  int32_t n;             /* N of the layer */
+  int32_t k;             /* K of the layer */
+  int32_t rows;          /* rows planned for: T*topk, M, or E*budget */
+  int32_t tok_e_x100;    /* routed rows per expert x 100, host estimate */
+  int32_t est_tiles;     /* M x N tiles expected without split-K */
+  int32_t profile;       /* qma_profile */
+  int32_t waves_k;       /* K partitions inside one workgroup */
+  int32_t reserved[2];
+} qma_plan_t;
+
+/* ---- layer (load time) ------------------------------------------------ */
+
+/* Checks the scheme and fixes the profile and the packed layout from
+ * (E, N, K) ([release] runtime considerations; [announce] scheduling and
+ * integration sections). N is the output width, K the reduction length.
+ * Errors: any scheme other than the accepted one -> QMA_ERR_UNSUPPORTED;
+ * E < 1, N % 16 != 0, K % 128 != 0, N or K < 1, a null pointer ->
+ * QMA_ERR_INVALID_ARG. The caller owns *out and frees it with
+ * qma_layer_destroy. */
+qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
+                            int32_t K, qma_path path, qma_layer_t** out);
+void qma_layer_destroy(qma_layer_t* layer);
+/* Reads back the shape, path and inferred profile. Null outputs are
+ * skipped. */
+qma_status qma_layer_info(const qma_layer_t* layer, int32_t* E, int32_t* N,
+                          int32_t* K, int32_t* path, int32_t* profile);
+
+/* Bytes of the packed weight buffer qma_prepack writes (weights + scales). */
+size_t qma_packed_weight_bytes(const qma_layer_t* layer);
+
+/* Load-time conversion of the checkpoint layout into the library's tiled
+ * layout ([announce] scheduling section: the weight layout is fixed when
+ * the model loads; [release] grouped techniques: weights packed in
+ * BLOCK_K = 128 chunks).
+ *   qweight [E, N, K/8] int32: 8 uint4 per word along K, nibble k%8 at bits
+ *           4*(k%8)..+3 (compressed-tensors pack-quantized INT4 group 32)
+ *   scales  [E, N, K/32] bf16
+ *   packed  qma_packed_weight_bytes(layer) bytes, 256-byte aligned
+ * All three are device buffers. The inputs are read and not kept. Errors:
+ * a null or misaligned pointer -> QMA_ERR_INVALID_ARG. */
+qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
+                       const uint16_t* scales, void* packed, void* stream);
+
+/* ---- planning (host only) --------------------------------------------- */
+
+/* Plan the indexed GEMM for T tokens routed top-`topk` over the layer's E
+ * experts. tok_e = T*topk/E picks block_m ([release] indexed techniques: a
+ * block-M heuristic keyed on routed tokens per expert, switching at 80),
+ * block_n comes from the tile count ([release] grouped techniques: the
+ * wider tile only when enough N tiles exist), and split-K turns on only
+ * when the grid would underfill the compute units ([release] indexed
+ * techniques: the stream-K gate). force_block_m = 0 lets the planner choose;
+ * otherwise it must be 16, 32, 48 or 64 (small-M) or 64, 128 or 256
+ * (large-M, when the planner picks large-M). The down projection passes
+ * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,
+ * a bad force_block_m, or a layer whose path is not INDEXED ->
+ * QMA_ERR_INVALID_ARG. */
+qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
+                            int32_t force_block_m, qma_plan_t* out);
+
+/* Plan a grouped GEMM. Contiguous layers: m_rows_or_budget = M, the padded
+ * row count (a multiple of 128), and expected_m is ignored. Masked layers:
+ * m_rows_or_budget = the per-expert row budget, and expected_m = the
+ * host-side estimate of valid rows that picks block_m ([release] grouped
+ * techniques: BLOCK_M from the expected token count). */
+qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
+                            int32_t expected_m, qma_plan_t* out);
+
+/* Bytes of fp32 split-K workspace the plan's GEMM needs (0 if split is off). */
+size_t qma_workspace_bytes(const qma_plan_t* plan);
+
+/* ---- routing ---------------------------------------------------------- */
+
+/* Capacities that always suffice for moe_align:
+ *   sorted_cap = T*topk + E*(block_m - 1);  blocks_cap = ceil(sorted_cap / block_m).
+ * Errors: negative T, topk < 1, E < 1, block_m < 1 -> QMA_ERR_INVALID_ARG. */
+qma_status qma_align_sizes(int32_t T, int32_t topk, int32_t E, int32_t block_m,
+                           int32_t* sorted_cap, int32_t* blocks_cap);
+
+/* Block-aligned routing buffers ([announce] scheduling section: the
+ * indexed path consumes sorted_ids / expert_ids / num_tokens_padded;
+ * [release] runtime considerations: over-allocated buffers).
+ * topk_ids [T, topk] int32 names each slot's expert; slot i = t*topk + k.
+ * Ids outside [0, E) mean "not on this rank" and are left out. Outputs:
+ *   sorted_ids [sorted_cap]: expert by expert in ascending order, the
+ *     expert's slots in ascending order, padded with the sentinel T*topk up
+ *     to a multiple of block_m; every entry past num_tokens_padded is the
+ *     sentinel;
+ *   expert_ids [ceil(sorted_cap/block_m)]: the expert of each block, -1
+ *     past the last;
+ *   num_tokens_padded [1]: the padded length.
+ * An expert with no slots gets no block. The result is deterministic
+ * (bit-exact). Errors: sorted_cap below the qma_align_sizes bound,
+ * E > 1024, T*topk >= 2^31 - E*block_m, or a null pointer ->
+ * QMA_ERR_INVALID_ARG. */
+qma_status qma_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk,
+                         int32_t E, int32_t block_m, int32_t* sorted_ids,
+                         int32_t* expert_ids, int32_t* num_tokens_padded,
+                         int32_t sorted_cap, void* stream);
+
+/* Routing validation, the opt-in check the trusted path skips ([release]
+ * runtime considerations). Reads the buffers back: it SYNCHRONISES the
+ * stream and is not capturable. It checks that the buffers are exactly
+ * what qma_moe_align defines for topk_ids, and that every id is in
+ * [-1, E). It returns QMA_ERR_ROUTING on the first violation, with detail
+ * text. */
+qma_status qma_validate_routing(const int32_t* topk_ids, int32_t T,
+                                int32_t topk, int32_t E, int32_t block_m,
+                                const int32_t* sorted_ids,
+                                const int32_t* expert_ids,
+                                const int32_t* num_tokens_padded,
+                                int32_t sorted_cap, void* stream);
+
+/* Checks a contiguous layout: every aligned 128-row block of m_indices
+ * [M] holds one expert id, then only -1, and ids are < E. Synchronises.
+ * Returns QMA_ERR_ROUTING on a violation. */
+qma_status qma_validate_contiguous(const int32_t* m_indices, int32_t M,
+                                   int32_t E, void* stream);
+
+/* ---- GEMMs ------------------------------------------------------------ */
+
+/* Indexed expert GEMM ([announce] scheduling section; [release] indexed
+ * techniques). For every block b < *num_tokens_padded / block_m with
+ * expert e = expert_ids[b], and every row s = sorted_ids[b*block_m + i]
+ * with s < num_slots:
+ *   c[s, n] = bf16( sum_k a[s / a_row_div, k] * (q_e[n,k] - 8) * scale_e[n, k/32] )
+ *             (times topk_weights[s] when topk_weights is not NULL)
+ * with fp32 accumulation. gate_up passes a_row_div = topk (the token's
+ * row); down passes 1 (the slot's own row of the activation output).
+ *   a        [a_rows, K] bf16
+ *   packed_w the layer's prepacked weights
+ *   routing  buffers from qma_moe_align with block_m = plan->block_m;
+ *            only device memory is read (no host sync), so the buffers may
+ *            be over-allocated up to sorted_cap
+ *   c        [num_slots, N] bf16; rows no block names are left untouched
+ *   ws       qma_workspace_bytes(plan) bytes of device memory, or NULL if 0
+ * Errors: a plan made for another layer shape or path, a null pointer, or
+ * a sorted_cap below the bound -> QMA_ERR_INVALID_ARG; a short workspace
+ * -> QMA_ERR_WORKSPACE. */
+qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
+                            const uint16_t* a, int32_t a_rows,
+                            int32_t a_row_div, const void* packed_w,
+                            const int32_t* sorted_ids,
+                            const int32_t* expert_ids,
+                            const int32_t* num_tokens_padded,
+                            int32_t sorted_cap, int32_t num_slots,
+                            const float* topk_weights, uint16_t* c, void* ws,
+                            size_t ws_bytes, void* stream);
+
+/* Grouped contiguous GEMM ([release] grouped techniques: contiguous
+ * prefill pads each expert to 128 rows). c[r] = a[r] . W[m_indices[r]]^T
+ * for rows with m_indices[r] >= 0.
+ *   a [M, K], m_indices [M] (device; -1 = padding), c [M, N];
+ *   M % 128 == 0. Padding rows of c are left untouched, and padding rows
+ *   of a are never read.
+ * The one-expert-per-128-row-block convention is checked only by
+ * qma_validate_contiguous. A row whose id differs from its block's first
+ * row is treated as padding. */
+qma_status qma_grouped_contiguous_gemm(const qma_layer_t* layer,
+                                       const qma_plan_t* plan,
+                                       const uint16_t* a,
+                                       const int32_t* m_indices, int32_t M,
+                                       const void* packed_w, uint16_t* c,
+                                       void* ws, size_t ws_bytes,
+                                       void* stream);
+
+/* Grouped masked GEMM ([release] grouped techniques: masked decode keeps
+ * a fixed row budget per expert). c[e, r] = a[e, r] . W[e]^T for
+ * r < masked_m[e].
+ *   a [E, Mb, K]; masked_m [E] is device memory, with values clamped to
+ *   [0, Mb]; c [E, Mb, N]. expected_m must equal the plan's.
+ * Rows r >= masked_m[e] are neither read nor written. */
+qma_status qma_grouped_masked_gemm(const qma_layer_t* layer,
+                                   const qma_plan_t* plan, const uint16_t* a,
+                                   const int32_t* masked_m, int32_t Mb,
+                                   int32_t expected_m, const void* packed_w,
+                                   uint16_t* c, void* ws, size_t ws_bytes,
+                                   void* stream);
+
+/* ---- activation and combine ------------------------------------------- */
+
+/* The gated activation between gate_up and down ([announce] measurement
+ * section names an activation between the two GEMMs; the gate is SiLU):
+ *   y[r, j] = bf16( silu(x[r, j]) * x[r, I + j] ), computed in fp32.
+ *   x [R, 2I] bf16 (gate half first), y [R, I] bf16.
+ * Errors: R < 0, I < 1, or a null pointer -> QMA_ERR_INVALID_ARG. */
+qma_status qma_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R,
+                            int32_t I, void* stream);
+
+/* Top-k combine after down (the step the pages leave out of the kernel
+ * timing): out[t, n] = bf16( sum_k w[t,k] * c2[t*topk + k, n] ), with fp32
+ * sums in k order. Slots whose expert id is outside [0, E) (NOT on this
+ * rank) are skipped when topk_ids is given.
+ *   c2 [T*topk, N] bf16, w [T, topk] fp32, topk_ids [T, topk] or NULL,
+ *   out [T, N] bf16. */
+qma_status qma_moe_combine(const uint16_t* c2, const float* w,
+                           const int32_t* topk_ids, int32_t E, int32_t T,
+                           int32_t topk, int32_t N, uint16_t* out,
+                           void* stream);
+
+/* ---- misc ------------------------------------------------------------- */
+
+const char* qma_status_str(qma_status s);
+/* Text of the last error on the calling thread ("" if none). */
+const char* qma_last_error_detail(void);
+/* Library version string. */
+const char* qma_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMA_H */

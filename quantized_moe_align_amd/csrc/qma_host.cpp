@@ -1,0 +1,562 @@
+// Host layer of libqma: status and error text, the quantisation-scheme
+// check, layers and their profile, the planner, argument validation and
+// the routing validators. Nothing here touches the GPU except the
+// validators' read-back and the calls into the launchers.
+//
+// Passages followed (see include/qma.h for the page titles):
+//   [release] runtime considerations: unsupported schemes fail at load; the
+//     EP/TP profile comes from the projection shapes with no shard args;
+//     the indexed kernels accept over-allocated routing buffers and are
+//     graph-capturable when routing validation is off.
+//   [release] indexed techniques: the tok_e block-M rule with threshold 80;
+//     the stream-K (here split-K) gate.
+//   [release] grouped techniques: BN256 only with enough N tiles (here the
+//     wider of two workgroup widths); BLOCK_M from the expected token
+//     count; a buffered K depth of about 512, up to about 768 for large
+//     masked tiles.
+//   [announce] scheduling section: the schedule follows routed tokens per
+//     expert; profile and layout are fixed at load.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "qma_internal.h"
+
+using qma::Layer;
+
+namespace {
+
+thread_local std::string g_detail;
+
+qma_status fail(qma_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+qma_status fail(qma_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_detail = buf;
+  return s;
+}
+
+qma_status ok() {
+  g_detail.clear();
+  return QMA_OK;
+}
+
+qma_status hip_status(int err, const char* what) {
+  if (err == 0) return ok();
+  return fail(QMA_ERR_HIP, "%s: %s", what, hipGetErrorString((hipError_t)err));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+int32_t infer_profile(int32_t E, int32_t N, int32_t K) {
+  (void)E;
+  // gate_up maps hidden -> 2*I (K >= N in every MoE share seen); down maps
+  // I -> hidden. A tensor-parallel share cuts I by the TP degree, so its
+  // hidden / I ratio is large; an expert-parallel share keeps I whole.
+  const bool gate_up = K >= N;
+  const int64_t I = gate_up ? N / 2 : K;
+  const int64_t H = gate_up ? K : N;
+  if (I <= 0) return QMA_PROFILE_GENERIC;
+  const bool tp = H >= 8 * I;
+  if (gate_up) return tp ? QMA_PROFILE_TP_GATE_UP : QMA_PROFILE_EP_GATE_UP;
+  return tp ? QMA_PROFILE_TP_DOWN : QMA_PROFILE_EP_DOWN;
+}
+
+int32_t ceil_div(int64_t a, int64_t b) { return (int32_t)((a + b - 1) / b); }
+
+void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
+  p->kernel = QMA_KERNEL_SMALL_M;
+  p->block_m = bm;
+  const int tm = bm / 16;
+  // The four waves of a workgroup split K when K is long (each wave still
+  // streams >= 8 chunks of 128) and split the columns otherwise.
+  int wk = L.k_chunks >= 32 ? 4 : (L.k_chunks >= 16 ? 2 : 1);
+  if (L.N % (16 * (4 / wk)) != 0) wk = 4;
+  const int wn = 4 / wk;
+  int ntw = 0;
+  for (int cand : {4, 2, 1})
+    if (!ntw && qma::small_m_supported(tm, cand) && L.N % (16 * wn * cand) == 0) ntw = cand;
+  // Wave-aware width: the narrower of the two widths when the wide one
+  // leaves CUs without a workgroup; an underfilled grid is then left to
+  // split-K.
+  if (ntw == 4 && (int64_t)tiles_m * (L.N / (16 * wn * 4)) < qma::kNumCUs &&
+      L.N % (16 * wn * 2) == 0)
+    ntw = 2;
+  p->waves_k = wk;
+  p->block_n = 16 * wn * ntw;
+  const int32_t tiles =
+      (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / p->block_n), 1 << 30);
+  p->est_tiles = tiles;
+  // Split-K gate: only when the grid underfills the CUs, and never below
+  // two 128-wide K chunks per wave.
+  int32_t split = 1;
+  if (tiles < qma::kNumCUs) {
+    const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / (2 * wk)));
+    split = std::min<int32_t>({ceil_div(qma::kNumCUs, std::max(tiles, 1)), max_split, 8});
+    split = std::max<int32_t>(split, 1);
+  }
+  p->split_k = split;
+  p->k_depth = qma::small_m_depth(tm, ntw) * qma::kChunkK;
+}
+
+void plan_common(const Layer& L, qma_plan_t* p) {
+  std::memset(p, 0, sizeof(*p));
+  p->path = L.path;
+  p->num_experts = L.E;
+  p->n = L.N;
+  p->k = L.K;
+  p->profile = L.profile;
+  p->split_k = 1;
+}
+
+// Activations are addressed with 32-bit buffer offsets.
+qma_status check_a_bytes(int64_t rows, int32_t K) {
+  if (rows * K * 2 >= (1ll << 31))
+    return fail(QMA_ERR_INVALID_ARG, "activation of %lld x %d bf16 exceeds 2 GiB; split the call",
+                (long long)rows, K);
+  return ok();
+}
+
+qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
+                            int32_t path) {
+  if (!layer || !plan) return fail(QMA_ERR_INVALID_ARG, "null layer or plan");
+  const Layer& L = layer->L;
+  if (L.path != path)
+    return fail(QMA_ERR_INVALID_ARG, "layer path %d does not match call (%d)",
+                L.path, path);
+  if (plan->path != L.path || plan->n != L.N || plan->k != L.K ||
+      plan->num_experts != L.E)
+    return fail(QMA_ERR_INVALID_ARG, "plan was made for another layer");
+  if (plan->kernel != QMA_KERNEL_SMALL_M && plan->kernel != QMA_KERNEL_LARGE_M)
+    return fail(QMA_ERR_INVALID_ARG, "plan has unknown kernel %d", plan->kernel);
+  if (plan->block_m < 16 || plan->block_m % 16 != 0 ||
+      (plan->kernel == QMA_KERNEL_SMALL_M && plan->block_m > 64))
+    return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
+  if (plan->split_k < 1 || plan->split_k > 8)
+    return fail(QMA_ERR_INVALID_ARG, "plan has bad split_k %d", plan->split_k);
+  if (plan->block_n != 16 && plan->block_n != 32 && plan->block_n != 64 &&
+      plan->block_n != 128 && plan->block_n != 256)
+    return fail(QMA_ERR_INVALID_ARG, "plan has bad block_n %d", plan->block_n);
+  if (L.N % plan->block_n != 0)
+    return fail(QMA_ERR_INVALID_ARG, "block_n %d does not divide N %d",
+                plan->block_n, L.N);
+  return ok();
+}
+
+size_t ws_bytes_for(const qma_plan_t* p, int64_t rows) {
+  if (p->split_k <= 1) return 0;
+  return (size_t)p->split_k * (size_t)rows * (size_t)p->n * sizeof(float);
+}
+
+qma_status check_ws(const qma_plan_t* plan, int64_t rows, const void* ws,
+                    size_t ws_bytes) {
+  const size_t need = ws_bytes_for(plan, rows);
+  if (need == 0) return ok();
+  if (!ws || ws_bytes < need)
+    return fail(QMA_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given",
+                need, ws ? ws_bytes : (size_t)0);
+  if (!aligned(ws, 16)) return fail(QMA_ERR_INVALID_ARG, "workspace not 16-byte aligned");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* qma_status_str(qma_status s) {
+  switch (s) {
+    case QMA_OK: return "QMA_OK";
+    case QMA_ERR_INVALID_ARG: return "QMA_ERR_INVALID_ARG";
+    case QMA_ERR_UNSUPPORTED: return "QMA_ERR_UNSUPPORTED";
+    case QMA_ERR_ROUTING: return "QMA_ERR_ROUTING";
+    case QMA_ERR_WORKSPACE: return "QMA_ERR_WORKSPACE";
+    case QMA_ERR_HIP: return "QMA_ERR_HIP";
+  }
+  return "QMA_ERR_UNKNOWN";
+}
+
+const char* qma_last_error_detail(void) { return g_detail.c_str(); }
+
+const char* qma_version(void) { return "qma 0.1 gfx950"; }
+
+qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
+                            int32_t K, qma_path path, qma_layer_t** out) {
+  if (!q || !out) return fail(QMA_ERR_INVALID_ARG, "null descriptor or out");
+  *out = nullptr;
+  if (q->weight_bits != 4)
+    return fail(QMA_ERR_UNSUPPORTED, "weight_bits %d: only uint4 is supported", q->weight_bits);
+  if (q->zero_point != 8)
+    return fail(QMA_ERR_UNSUPPORTED, "zero_point %d: only 8 is supported", q->zero_point);
+  if (q->group_size != 32)
+    return fail(QMA_ERR_UNSUPPORTED, "group_size %d: only 32 is supported", q->group_size);
+  if (q->scale_dtype != QMA_DTYPE_BF16)
+    return fail(QMA_ERR_UNSUPPORTED, "scale dtype %d: only bf16 scales are supported", q->scale_dtype);
+  if (q->act_dtype != QMA_DTYPE_BF16)
+    return fail(QMA_ERR_UNSUPPORTED, "activation dtype %d: only bf16 is supported", q->act_dtype);
+  if (q->pack_format != QMA_PACK_INT32_K8)
+    return fail(QMA_ERR_UNSUPPORTED, "pack format %d: only int32 K8 is supported", q->pack_format);
+  if (path != QMA_PATH_INDEXED && path != QMA_PATH_GROUPED_CONTIGUOUS &&
+      path != QMA_PATH_GROUPED_MASKED)
+    return fail(QMA_ERR_INVALID_ARG, "unknown path %d", (int)path);
+  if (E < 1 || N < 16 || K < 128)
+    return fail(QMA_ERR_INVALID_ARG, "bad shape E=%d N=%d K=%d", E, N, K);
+  if (N % 16 != 0) return fail(QMA_ERR_INVALID_ARG, "N=%d is not a multiple of 16", N);
+  if (K % 128 != 0) return fail(QMA_ERR_INVALID_ARG, "K=%d is not a multiple of 128", K);
+  auto* l = new (std::nothrow) qma_layer_t;
+  if (!l) return fail(QMA_ERR_INVALID_ARG, "out of host memory");
+  Layer& L = l->L;
+  L.E = E;
+  L.N = N;
+  L.K = K;
+  L.path = path;
+  L.profile = infer_profile(E, N, K);
+  L.n_tiles = N / qma::kTileN;
+  L.k_chunks = K / qma::kChunkK;
+  L.w_bytes = (size_t)E * L.n_tiles * L.k_chunks * qma::kWBlockBytes;
+  L.s_bytes = (size_t)E * L.n_tiles * L.k_chunks * qma::kSBlockBytes;
+  *out = l;
+  return ok();
+}
+
+void qma_layer_destroy(qma_layer_t* layer) { delete layer; }
+
+qma_status qma_layer_info(const qma_layer_t* layer, int32_t* E, int32_t* N,
+                          int32_t* K, int32_t* path, int32_t* profile) {
+  if (!layer) return fail(QMA_ERR_INVALID_ARG, "null layer");
+  if (E) *E = layer->L.E;
+  if (N) *N = layer->L.N;
+  if (K) *K = layer->L.K;
+  if (path) *path = layer->L.path;
+  if (profile) *profile = layer->L.profile;
+  return ok();
+}
+
+size_t qma_packed_weight_bytes(const qma_layer_t* layer) {
+  if (!layer) return 0;
+  return layer->L.w_bytes + layer->L.s_bytes;
+}
+
+qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
+                       const uint16_t* scales, void* packed, void* stream) {
+  if (!layer || !qweight || !scales || !packed)
+    return fail(QMA_ERR_INVALID_ARG, "null argument");
+  if (!aligned(packed, 256)) return fail(QMA_ERR_INVALID_ARG, "packed buffer not 256-byte aligned");
+  if (!aligned(qweight, 4) || !aligned(scales, 2))
+    return fail(QMA_ERR_INVALID_ARG, "misaligned qweight or scales");
+  return hip_status(qma::launch_prepack(layer->L, qweight, scales, packed, stream),
+                    "prepack launch");
+}
+
+qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
+                            int32_t force_block_m, qma_plan_t* out) {
+  if (!layer || !out) return fail(QMA_ERR_INVALID_ARG, "null layer or out");
+  const Layer& L = layer->L;
+  if (L.path != QMA_PATH_INDEXED) return fail(QMA_ERR_INVALID_ARG, "layer is not INDEXED");
+  if (T < 0 || topk < 1) return fail(QMA_ERR_INVALID_ARG, "bad T=%d topk=%d", T, topk);
+  const int64_t R = (int64_t)T * topk;
+  if (R >= (1ll << 30)) return fail(QMA_ERR_INVALID_ARG, "T*topk too large");
+  plan_common(L, out);
+  out->rows = (int32_t)R;
+  const double tok_e = (double)R / L.E;
+  out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
+  int32_t bm;
+  if (force_block_m != 0) {
+    if (force_block_m != 16 && force_block_m != 32 && force_block_m != 64)
+      return fail(QMA_ERR_INVALID_ARG, "force_block_m %d not in {16,32,64}", force_block_m);
+    bm = force_block_m;
+  } else {
+    // Below 80 routed rows per expert: the smallest of 16, 32, 64 >= tok_e.
+    bm = tok_e <= 16 ? 16 : (tok_e <= 32 ? 32 : 64);
+  }
+  const int64_t e_active = std::min<int64_t>(L.E, std::max<int64_t>(R, 1));
+  const int64_t per_e = std::max<int64_t>(1, ceil_div((int64_t)std::ceil(tok_e), bm));
+  plan_small_m(L, bm, (int32_t)std::min<int64_t>(e_active * per_e, 1 << 30), out);
+  return ok();
+}
+
+qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
+                            int32_t expected_m, qma_plan_t* out) {
+  if (!layer || !out) return fail(QMA_ERR_INVALID_ARG, "null layer or out");
+  const Layer& L = layer->L;
+  plan_common(L, out);
+  if (L.path == QMA_PATH_GROUPED_CONTIGUOUS) {
+    const int32_t M = m_rows_or_budget;
+    if (M < 0 || M % 128 != 0)
+      return fail(QMA_ERR_INVALID_ARG, "contiguous M=%d is not a multiple of 128", M);
+    out->rows = M;
+    const double tok_e = (double)M / L.E;
+    out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
+    plan_small_m(L, 64, std::max(1, M / 64), out);
+    return ok();
+  }
+  if (L.path == QMA_PATH_GROUPED_MASKED) {
+    const int32_t Mb = m_rows_or_budget;
+    if (Mb < 1 || expected_m < 0 || expected_m > Mb)
+      return fail(QMA_ERR_INVALID_ARG, "bad budget %d / expected_m %d", Mb, expected_m);
+    if ((int64_t)Mb * L.E >= (1ll << 30)) return fail(QMA_ERR_INVALID_ARG, "E*budget too large");
+    out->rows = Mb * L.E;
+    out->tok_e_x100 = expected_m * 100;
+    const int32_t bm = expected_m <= 16 ? 16 : (expected_m <= 32 ? 32 : 64);
+    plan_small_m(L, bm, L.E * std::max(1, ceil_div(std::max(expected_m, 1), bm)), out);
+    out->reserved[0] = expected_m;
+    return ok();
+  }
+  return fail(QMA_ERR_INVALID_ARG, "layer is not a grouped layer");
+}
+
+size_t qma_workspace_bytes(const qma_plan_t* plan) {
+  if (!plan) return 0;
+  return ws_bytes_for(plan, plan->rows);
+}
+
+qma_status qma_align_sizes(int32_t T, int32_t topk, int32_t E, int32_t block_m,
+                           int32_t* sorted_cap, int32_t* blocks_cap) {
+  if (T < 0 || topk < 1 || E < 1 || block_m < 1)
+    return fail(QMA_ERR_INVALID_ARG, "bad T=%d topk=%d E=%d block_m=%d", T, topk, E, block_m);
+  const int64_t cap = (int64_t)T * topk + (int64_t)E * (block_m - 1);
+  if (cap >= (1ll << 31) - block_m) return fail(QMA_ERR_INVALID_ARG, "capacity overflows int32");
+  if (sorted_cap) *sorted_cap = (int32_t)cap;
+  if (blocks_cap) *blocks_cap = (int32_t)((cap + block_m - 1) / block_m);
+  return ok();
+}
+
+qma_status qma_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk,
+                         int32_t E, int32_t block_m, int32_t* sorted_ids,
+                         int32_t* expert_ids, int32_t* num_tokens_padded,
+                         int32_t sorted_cap, void* stream) {
+  int32_t need = 0;
+  qma_status s = qma_align_sizes(T, topk, E, block_m, &need, nullptr);
+  if (s != QMA_OK) return s;
+  if (E > qma::kMaxExperts) return fail(QMA_ERR_INVALID_ARG, "E=%d exceeds %d", E, qma::kMaxExperts);
+  if (sorted_cap < need)
+    return fail(QMA_ERR_INVALID_ARG, "sorted_cap %d below the bound %d", sorted_cap, need);
+  if ((T > 0 && !topk_ids) || !sorted_ids || !expert_ids || !num_tokens_padded)
+    return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  return hip_status(qma::launch_moe_align(topk_ids, T * topk, E, block_m, sorted_ids,
+                                          expert_ids, num_tokens_padded, sorted_cap,
+                                          stream),
+                    "moe_align launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+template <typename T>
+qma_status read_back(std::vector<T>& dst, const T* src, size_t n, hipStream_t st) {
+  dst.resize(n);
+  if (n == 0) return ok();
+  hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return hip_status((int)e, "validation read-back");
+}
+
+}  // namespace
+
+extern "C" {
+
+qma_status qma_validate_routing(const int32_t* topk_ids, int32_t T, int32_t topk,
+                                int32_t E, int32_t block_m,
+                                const int32_t* sorted_ids, const int32_t* expert_ids,
+                                const int32_t* num_tokens_padded, int32_t sorted_cap,
+                                void* stream) {
+  if (T < 0 || topk < 1 || E < 1 || block_m < 1 || sorted_cap < 0)
+    return fail(QMA_ERR_INVALID_ARG, "bad sizes");
+  if ((T > 0 && !topk_ids) || !sorted_ids || !expert_ids || !num_tokens_padded)
+    return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  hipStream_t st = (hipStream_t)stream;
+  const int64_t R = (int64_t)T * topk;
+  const int64_t blocks = (sorted_cap + block_m - 1) / block_m;
+  std::vector<int32_t> ids, sorted, experts, ntp;
+  qma_status s;
+  if ((s = read_back(ids, topk_ids, (size_t)R, st)) != QMA_OK) return s;
+  if ((s = read_back(sorted, sorted_ids, (size_t)sorted_cap, st)) != QMA_OK) return s;
+  if ((s = read_back(experts, expert_ids, (size_t)blocks, st)) != QMA_OK) return s;
+  if ((s = read_back(ntp, num_tokens_padded, 1, st)) != QMA_OK) return s;
+  for (int64_t i = 0; i < R; ++i)
+    if (ids[i] < -1 || ids[i] >= E)
+      return fail(QMA_ERR_ROUTING, "topk_ids[%lld] = %d outside [-1, %d)", (long long)i, ids[i], E);
+  const int64_t n = ntp[0];
+  if (n < 0 || n > sorted_cap || n % block_m != 0)
+    return fail(QMA_ERR_ROUTING, "num_tokens_padded %lld invalid (cap %d, block %d)",
+                (long long)n, sorted_cap, block_m);
+  std::vector<int32_t> seen((size_t)R, 0);
+  for (int64_t p = 0; p < n; ++p) {
+    const int32_t e = experts[p / block_m];
+    if (e < 0 || e >= E)
+      return fail(QMA_ERR_ROUTING, "expert_ids[%lld] = %d outside [0, %d)", (long long)(p / block_m), e, E);
+    const int32_t sl = sorted[p];
+    if (sl < 0) return fail(QMA_ERR_ROUTING, "sorted_ids[%lld] = %d negative", (long long)p, sl);
+    if (sl >= R) continue;  // padding
+    if (ids[sl] != e)
+      return fail(QMA_ERR_ROUTING, "sorted_ids[%lld] = slot %d of expert %d placed in a block of expert %d",
+                  (long long)p, sl, ids[sl], e);
+    if (seen[sl]++)
+      return fail(QMA_ERR_ROUTING, "slot %d appears twice", sl);
+  }
+  for (int64_t i = 0; i < R; ++i)
+    if (ids[i] >= 0 && !seen[i])
+      return fail(QMA_ERR_ROUTING, "slot %lld (expert %d) is missing", (long long)i, ids[i]);
+  return ok();
+}
+
+qma_status qma_validate_contiguous(const int32_t* m_indices, int32_t M, int32_t E,
+                                   void* stream) {
+  if (M < 0 || M % 128 != 0 || E < 1) return fail(QMA_ERR_INVALID_ARG, "bad M=%d or E=%d", M, E);
+  if (M > 0 && !m_indices) return fail(QMA_ERR_INVALID_ARG, "null m_indices");
+  std::vector<int32_t> m;
+  qma_status s = read_back(m, m_indices, (size_t)M, (hipStream_t)stream);
+  if (s != QMA_OK) return s;
+  for (int32_t b = 0; b < M; b += 128) {
+    const int32_t e = m[b];
+    if (e < -1 || e >= E) return fail(QMA_ERR_ROUTING, "m_indices[%d] = %d outside [-1, %d)", b, e, E);
+    bool pad = e < 0;
+    for (int32_t r = b; r < b + 128; ++r) {
+      if (m[r] == -1) { pad = true; continue; }
+      if (pad || m[r] != e)
+        return fail(QMA_ERR_ROUTING, "m_indices[%d] = %d breaks the one-expert 128-row block at %d",
+                    r, m[r], b);
+    }
+  }
+  return ok();
+}
+
+qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
+                            const uint16_t* a, int32_t a_rows, int32_t a_row_div,
+                            const void* packed_w, const int32_t* sorted_ids,
+                            const int32_t* expert_ids, const int32_t* num_tokens_padded,
+                            int32_t sorted_cap, int32_t num_slots,
+                            const float* topk_weights, uint16_t* c, void* ws,
+                            size_t ws_bytes, void* stream) {
+  qma_status s = check_layer_plan(layer, plan, QMA_PATH_INDEXED);
+  if (s != QMA_OK) return s;
+  if (a_rows < 0 || a_row_div < 1 || num_slots < 0 || sorted_cap < 0)
+    return fail(QMA_ERR_INVALID_ARG, "bad sizes");
+  if ((int64_t)a_rows * a_row_div < num_slots)
+    return fail(QMA_ERR_INVALID_ARG, "a has %d rows; %d slots / %d need more", a_rows,
+                num_slots, a_row_div);
+  if (!a || !packed_w || !sorted_ids || !expert_ids || !num_tokens_padded || !c)
+    return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(a, 16) || !aligned(c, 16) || !aligned(packed_w, 256))
+    return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
+  if ((s = check_ws(plan, num_slots, ws, ws_bytes)) != QMA_OK) return s;
+  if ((s = check_a_bytes(a_rows, layer->L.K)) != QMA_OK) return s;
+  if (sorted_cap == 0 || num_slots == 0) return ok();
+  qma::GemmArgs g{};
+  g.layer = &layer->L;
+  g.plan = plan;
+  g.a = a;
+  g.packed = packed_w;
+  g.c = c;
+  g.ws = ws;
+  g.mode = 0;
+  g.a_row_div = a_row_div;
+  g.sorted_ids = sorted_ids;
+  g.expert_ids = expert_ids;
+  g.ntp = num_tokens_padded;
+  g.num_tiles = (sorted_cap + plan->block_m - 1) / plan->block_m;
+  g.num_slots = num_slots;
+  g.topk_weights = topk_weights;
+  g.rows_cap = num_slots;
+  g.sorted_cap = sorted_cap;
+  g.a_bytes = (int64_t)a_rows * layer->L.K * 2;
+  return hip_status(qma::launch_gemm(g, stream), "indexed gemm launch");
+}
+
+qma_status qma_grouped_contiguous_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
+                                       const uint16_t* a, const int32_t* m_indices,
+                                       int32_t M, const void* packed_w, uint16_t* c,
+                                       void* ws, size_t ws_bytes, void* stream) {
+  qma_status s = check_layer_plan(layer, plan, QMA_PATH_GROUPED_CONTIGUOUS);
+  if (s != QMA_OK) return s;
+  if (M < 0 || M % 128 != 0) return fail(QMA_ERR_INVALID_ARG, "M=%d not a multiple of 128", M);
+  if (128 % plan->block_m != 0)
+    return fail(QMA_ERR_INVALID_ARG, "block_m %d does not divide 128", plan->block_m);
+  if (M > plan->rows) return fail(QMA_ERR_INVALID_ARG, "M=%d exceeds the plan's %d rows", M, plan->rows);
+  if (!a || !m_indices || !packed_w || !c) return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(a, 16) || !aligned(c, 16) || !aligned(packed_w, 256))
+    return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
+  if ((s = check_ws(plan, M, ws, ws_bytes)) != QMA_OK) return s;
+  if ((s = check_a_bytes(M, layer->L.K)) != QMA_OK) return s;
+  if (M == 0) return ok();
+  qma::GemmArgs g{};
+  g.layer = &layer->L;
+  g.plan = plan;
+  g.a = a;
+  g.packed = packed_w;
+  g.c = c;
+  g.ws = ws;
+  g.mode = 1;
+  g.a_row_div = 1;
+  g.m_indices = m_indices;
+  g.num_tiles = M / plan->block_m;
+  g.num_slots = M;
+  g.rows_cap = M;
+  g.a_bytes = (int64_t)M * layer->L.K * 2;
+  return hip_status(qma::launch_gemm(g, stream), "contiguous gemm launch");
+}
+
+qma_status qma_grouped_masked_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
+                                   const uint16_t* a, const int32_t* masked_m, int32_t Mb,
+                                   int32_t expected_m, const void* packed_w, uint16_t* c,
+                                   void* ws, size_t ws_bytes, void* stream) {
+  qma_status s = check_layer_plan(layer, plan, QMA_PATH_GROUPED_MASKED);
+  if (s != QMA_OK) return s;
+  if (Mb < 1 || (int64_t)Mb * layer->L.E != plan->rows)
+    return fail(QMA_ERR_INVALID_ARG, "budget %d does not match the plan", Mb);
+  if (expected_m != plan->reserved[0])
+    return fail(QMA_ERR_INVALID_ARG, "expected_m %d does not match the plan's %d", expected_m,
+                plan->reserved[0]);
+  if (!a || !masked_m || !packed_w || !c) return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(a, 16) || !aligned(c, 16) || !aligned(packed_w, 256))
+    return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
+  if ((s = check_ws(plan, (int64_t)Mb * layer->L.E, ws, ws_bytes)) != QMA_OK) return s;
+  if ((s = check_a_bytes((int64_t)Mb * layer->L.E, layer->L.K)) != QMA_OK) return s;
+  qma::GemmArgs g{};
+  g.layer = &layer->L;
+  g.plan = plan;
+  g.a = a;
+  g.packed = packed_w;
+  g.c = c;
+  g.ws = ws;
+  g.mode = 2;
+  g.a_row_div = 1;
+  g.masked_m = masked_m;
+  g.Mb = Mb;
+  g.tiles_per_expert = (Mb + plan->block_m - 1) / plan->block_m;
+  g.num_tiles = g.tiles_per_expert * layer->L.E;
+  g.num_slots = Mb * layer->L.E;
+  g.rows_cap = Mb * layer->L.E;
+  g.a_bytes = (int64_t)Mb * layer->L.E * layer->L.K * 2;
+  return hip_status(qma::launch_gemm(g, stream), "masked gemm launch");
+}
+
+qma_status qma_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I,
+                            void* stream) {
+  if (R < 0 || I < 1) return fail(QMA_ERR_INVALID_ARG, "bad R=%lld I=%d", (long long)R, I);
+  if (R == 0) return ok();
+  if (!x || !y) return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  return hip_status(qma::launch_silu_and_mul(x, y, R, I, stream), "silu_and_mul launch");
+}
+
+qma_status qma_moe_combine(const uint16_t* c2, const float* w, const int32_t* topk_ids,
+                           int32_t E, int32_t T, int32_t topk, int32_t N, uint16_t* out,
+                           void* stream) {
+  if (T < 0 || topk < 1 || N < 1 || (topk_ids && E < 1))
+    return fail(QMA_ERR_INVALID_ARG, "bad sizes");
+  if (T == 0) return ok();
+  if (!c2 || !w || !out) return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  return hip_status(qma::launch_combine(c2, w, topk_ids, E, T, topk, N, out, stream),
+                    "combine launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,104 @@
+// Internal declarations shared by the host layer (qma_host.cpp) and the
+// kernels (qma_kernels.hip). Not part of the public ABI.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/qma.h"
+
+// Packed layout (fixed at load). For expert e, 16-row tile nt, and 128-wide
+// K chunk kc, one 1 KiB block holds the uint4 values in MFMA fragment order:
+// lane l (0..63) owns 16 bytes = 4 words; word j covers row nt*16 + l%16,
+// K range kc*128 + j*32 + (l/16)*8 .. +7. Inside a word the eight values sit
+// in the order (k0, k2, k4, k6, k1, k3, k5, k7) from the low nibble up, so
+// that (w >> 4p) & 0x000F000F isolates the pair (k2p, k2p+1), one per
+// 16-bit half. A second region holds the scales: per (e, nt, kc) 128 bytes
+// laid out [16 rows][4 groups] bf16.
+namespace qma {
+
+constexpr int kTileN = 16;       // weight rows per MFMA tile
+constexpr int kChunkK = 128;     // K elements per packed chunk
+constexpr int kGroup = 32;       // K elements per scale
+constexpr int kWBlockBytes = 1024;
+constexpr int kSBlockBytes = 128;
+constexpr int kMaxExperts = 1024;  // moe_align's single-workgroup limit
+constexpr int kNumCUs = 256;
+
+struct Layer {
+  int32_t E, N, K;
+  int32_t path;
+  int32_t profile;
+  int64_t n_tiles;     // N / 16
+  int64_t k_chunks;    // K / 128
+  size_t w_bytes;      // weight region
+  size_t s_bytes;      // scale region
+};
+
+inline size_t w_block_offset(const Layer& L, int64_t e, int64_t nt, int64_t kc) {
+  return (size_t)(((e * L.n_tiles + nt) * L.k_chunks + kc) * kWBlockBytes);
+}
+
+// Arguments the GEMM launchers take, after host validation.
+struct GemmArgs {
+  const Layer* layer;
+  const qma_plan_t* plan;
+  const uint16_t* a;
+  const void* packed;
+  uint16_t* c;
+  void* ws;
+  // row mapping
+  int32_t mode;              // 0 indexed, 1 contiguous, 2 masked
+  int32_t a_row_div;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* ntp;
+  int32_t num_tiles;         // token tiles in the grid (before padding)
+  int32_t num_slots;
+  const float* topk_weights;
+  const int32_t* m_indices;
+  const int32_t* masked_m;
+  int32_t Mb;                // masked budget
+  int32_t tiles_per_expert;  // masked
+  int32_t rows_cap;          // rows of the split-K workspace
+  int32_t sorted_cap;        // entries of sorted_ids (indexed)
+  int64_t a_bytes;           // bytes of the activation buffer
+};
+
+// Launchers (qma_kernels.hip). Each returns a hipError_t as int.
+int launch_moe_align(const int32_t* ids, int32_t R, int32_t E, int32_t B,
+                     int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                     int32_t cap, void* stream);
+int launch_prepack(const Layer& L, const int32_t* qweight,
+                   const uint16_t* scales, void* packed, void* stream);
+int launch_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I,
+                        void* stream);
+int launch_gemm(const GemmArgs& g, void* stream);
+int launch_combine(const uint16_t* c2, const float* w, const int32_t* ids,
+                   int32_t E, int32_t T, int32_t topk, int32_t N,
+                   uint16_t* out, void* stream);
+
+}  // namespace qma
+
+struct qma_layer {
+  qma::Layer L;
+};
+
+namespace qma {
+// Small-M kernel instances: TM = 16-token tiles per workgroup (1, 2 or 4),
+// NTW = 16-column weight tiles per wave (1, 2 or 4). A workgroup has 4 waves;
+// waves_k of them split K and 4 / waves_k split the columns, so
+// block_n = 16 * NTW * (4 / waves_k). The cross-wave reduction holds up to
+// 4 x NTW x TM KiB of LDS, so TM * NTW <= 8. The prefetch depth (128-wide K
+// chunks in flight per wave) is sized to a ~200 VGPR budget.
+constexpr bool small_m_supported(int tm, int ntw) {
+  return (tm == 1 || tm == 2 || tm == 4) && (ntw == 1 || ntw == 2 || ntw == 4) &&
+         tm * ntw <= 8;
+}
+constexpr int small_m_depth(int tm, int ntw) {
+  const int per = ntw * 6 + tm * 16;
+  const int fixed = ntw * tm * 4 + tm * 4 + 30;
+  const int d = (200 - fixed) / per;
+  return d < 2 ? 2 : (d > 4 ? 4 : d);
+}
+}  // namespace qma

@@ -1,0 +1,725 @@
+// HIP kernels of libqma for gfx950 (CDNA4): block-aligned routing
+// (moe_align), weight prepack, the W4A16 expert GEMMs, the split-K
+// reduction, the SiLU-gated activation and the top-k combine.
+//
+// The passages followed are cited per kernel (page titles in include/qma.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+
+#include "qma_internal.h"
+
+namespace qma {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // fp32 -> bf16, round to nearest even (v_cvt_pk_bf16_f32).
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
+
+// ---------------------------------------------------------------------------
+// moe_align: stable counting sort of routed slots by expert, each expert
+// padded to a multiple of the block size ([announce] scheduling section; the
+// buffers may be over-allocated: [release] runtime considerations).
+//
+// One workgroup of 8 waves. Wave w owns a contiguous range of slots. Pass 1
+// counts slots per (wave, expert) in LDS. A scan turns the counts into
+// per-(wave, expert) start positions that follow expert order, then wave
+// order, so positions ascend with the slot index. Pass 2 walks each wave's
+// range in 64-slot steps. A lane's rank among the lanes holding the same
+// expert comes from ballots over the expert id's bits, which keeps the
+// within-step order by lane. The result is deterministic and needs no
+// global atomics.
+// ---------------------------------------------------------------------------
+constexpr int kAlignWaves = 8;
+constexpr int kAlignThreads = kAlignWaves * 64;
+
+__global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
+    const int32_t* __restrict__ ids, int32_t R, int32_t E, int32_t B,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ expert_ids,
+    int32_t* __restrict__ ntp_out, int32_t cap, int32_t blocks_cap) {
+  extern __shared__ int32_t smem[];
+  int32_t* wc = smem;                       // [waves][E]
+  int32_t* cnt = wc + kAlignWaves * E;      // [E]
+  int32_t* off = cnt + E;                   // [E + 1]
+  int32_t* wsum = off + E + 1;              // [waves]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wc[i] = 0;
+  __syncthreads();
+  const int per = (R + kAlignWaves - 1) / kAlignWaves;
+  const int lo = min(R, w * per), hi = min(R, lo + per);
+  for (int i = lo + lane; i < hi; i += 64) {
+    const int e = ids[i];
+    if ((unsigned)e < (unsigned)E) atomicAdd(&wc[w * E + e], 1);
+  }
+  __syncthreads();
+  // per expert: total, and exclusive prefix over waves (in place)
+  for (int e = tid; e < E; e += kAlignThreads) {
+    int run = 0;
+    for (int v = 0; v < kAlignWaves; ++v) {
+      const int c = wc[v * E + e];
+      wc[v * E + e] = run;
+      run += c;
+    }
+    cnt[e] = run;
+  }
+  __syncthreads();
+  // exclusive scan of padded counts over experts; each thread takes a
+  // contiguous run of experts (E <= 1024 -> at most 2 per thread)
+  const int ept = (E + kAlignThreads - 1) / kAlignThreads;
+  const int e0 = min(E, tid * ept), e1 = min(E, e0 + ept);
+  int local = 0;
+  for (int e = e0; e < e1; ++e) local += (cnt[e] + B - 1) / B * B;
+  int incl = local;
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += t;
+  }
+  if (lane == 63) wsum[w] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  for (int v = 0; v < w; ++v) wave_base += wsum[v];
+  int run = wave_base + incl - local;
+  for (int e = e0; e < e1; ++e) {
+    off[e] = run;
+    run += (cnt[e] + B - 1) / B * B;
+  }
+  if (tid == kAlignThreads - 1) off[E] = run;
+  __syncthreads();
+  const int ntp = off[E];
+  if (tid == 0) *ntp_out = ntp;
+  for (int i = tid; i < kAlignWaves * E; i += kAlignThreads) wc[i] += off[i % E];
+  // expert of each block (binary search in the offsets), -1 past the end
+  for (int b = tid; b < blocks_cap; b += kAlignThreads) {
+    const int p = b * B;
+    int e = -1;
+    if (p < ntp) {
+      int l = 0, h = E - 1;  // largest e with off[e] <= p
+      while (l < h) {
+        const int m = (l + h + 1) >> 1;
+        if (off[m] <= p) l = m; else h = m - 1;
+      }
+      e = l;
+    }
+    expert_ids[b] = e;
+  }
+  // sentinel padding inside each expert's segment, and the tail
+  for (int e = tid; e < E; e += kAlignThreads)
+    for (int p = off[e] + cnt[e]; p < off[e + 1]; ++p) sorted_ids[p] = R;
+  for (int p = ntp + tid; p < cap; p += kAlignThreads) sorted_ids[p] = R;
+  __syncthreads();
+  // pass 2: place each slot
+  const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const int e = (i < hi) ? ids[i] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    uint64_t peers = __ballot(valid);
+    for (int bit = 0; bit < nbits; ++bit) {
+      const bool set = valid && ((e >> bit) & 1);
+      const uint64_t m = __ballot(set);
+      peers &= set ? m : ~m;
+    }
+    const int rank = __popcll(peers & below);
+    int pos = 0;
+    if (valid) pos = wc[w * E + e];
+    if (valid) sorted_ids[pos + rank] = i;
+    if (valid && (peers & below) == 0) wc[w * E + e] = pos + __popcll(peers);
+  }
+}
+
+int launch_moe_align(const int32_t* ids, int32_t R, int32_t E, int32_t B,
+                     int32_t* sorted_ids, int32_t* expert_ids, int32_t* ntp,
+                     int32_t cap, void* stream) {
+  const int32_t blocks_cap = (cap + B - 1) / B;
+  const size_t lds = sizeof(int32_t) * ((size_t)kAlignWaves * E + E + E + 1 + kAlignWaves);
+  hipLaunchKernelGGL(moe_align_kernel, dim3(1), dim3(kAlignThreads), lds,
+                     (hipStream_t)stream, ids, R, E, B, sorted_ids, expert_ids, ntp, cap,
+                     blocks_cap);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// prepack: checkpoint layout -> MFMA-fragment-ordered 128-wide K chunks
+// (layout fixed at load: [announce] scheduling section; BLOCK_K = 128
+// packing: [release] grouped techniques). See qma_internal.h for the layout.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t interleave_nibbles(uint32_t w) {
+  // out nibble p <- in nibble {0,2,4,6,1,3,5,7}[p]
+  uint32_t r = 0;
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int src = (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+    r |= ((w >> (4 * src)) & 0xFu) << (4 * p);
+  }
+  return r;
+}
+
+__global__ void prepack_weights_kernel(const uint32_t* __restrict__ qw, uint32_t* __restrict__ out,
+                                       int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
+                                       int64_t total) {
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int j = (int)(o & 3);
+    const int l = (int)((o >> 2) & 63);
+    int64_t rest = o >> 8;
+    const int64_t kc = rest % k_chunks;
+    rest /= k_chunks;
+    const int64_t nt = rest % n_tiles;
+    const int64_t e = rest / n_tiles;
+    const int64_t n = nt * 16 + (l & 15);
+    const int64_t k0 = kc * 128 + j * 32 + (l >> 4) * 8;
+    out[o] = interleave_nibbles(qw[(e * N + n) * (K / 8) + k0 / 8]);
+  }
+}
+
+__global__ void prepack_scales_kernel(const uint16_t* __restrict__ sc, uint16_t* __restrict__ out,
+                                      int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
+                                      int64_t total) {
+  for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
+       o += (int64_t)gridDim.x * blockDim.x) {
+    const int g = (int)(o & 3);
+    const int row = (int)((o >> 2) & 15);
+    int64_t rest = o >> 6;
+    const int64_t kc = rest % k_chunks;
+    rest /= k_chunks;
+    const int64_t nt = rest % n_tiles;
+    const int64_t e = rest / n_tiles;
+    const int64_t n = nt * 16 + row;
+    out[o] = sc[(e * N + n) * (K / 32) + kc * 4 + g];
+  }
+}
+
+int launch_prepack(const Layer& L, const int32_t* qweight, const uint16_t* scales,
+                   void* packed, void* stream) {
+  const int64_t words = (int64_t)(L.w_bytes / 4);
+  const int64_t svals = (int64_t)(L.s_bytes / 2);
+  auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
+  hipLaunchKernelGGL(prepack_weights_kernel, dim3(blocks(words)), dim3(256), 0,
+                     (hipStream_t)stream, (const uint32_t*)qweight, (uint32_t*)packed, L.N, L.K,
+                     L.n_tiles, L.k_chunks, words);
+  hipLaunchKernelGGL(prepack_scales_kernel, dim3(blocks(svals)), dim3(256), 0,
+                     (hipStream_t)stream, scales, (uint16_t*)((char*)packed + L.w_bytes), L.N,
+                     L.K, L.n_tiles, L.k_chunks, svals);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Small-M expert GEMM (decode shapes: 16 to 64 rows per tile).
+//
+// One v_mfma_f32_16x16x32_bf16 takes 16 tokens as its rows and 16 weight
+// rows (output columns) as its columns, and covers exactly one 32-wide
+// scale group. Each lane then owns one output column and needs one scale
+// per group. Both MFMA dimensions are 16 on CDNA4, so a handful of tokens
+// per expert fills the matrix core without exchanging operand roles. (The
+// pages' decode kernel puts weights on the MMA M side because its MMA is
+// 16x8: [announce] scheduling section.)
+//
+// The weight operand is the exact bf16 value 128+q, made from the nibbles
+// by an and-or, so dequantisation never rounds. The zero point enters
+// through the accumulator input: an MFMA against a constant -136 operand
+// gives -136 * sum_k x_k, so each MFMA yields sum_k x_k (q_k - 8), and the
+// group's scale is applied in fp32:
+//     acc += scale[n, g] * ( sum_k x_k (128 + q_k) - 136 sum_k x_k ).
+//
+// Workgroup: 4 waves. WK of them split the workgroup's K range and 4/WK
+// split its columns. A wave owns NTW 16-column weight tiles and TM 16-token
+// tiles. It streams its weights with buffer loads: per 128-wide K chunk, a
+// 1 KiB contiguous block per tile, with D chunks in flight. Token rows are
+// gathered with buffer loads whose out-of-range offset returns zeros for
+// rows the tile does not use, so those rows are never read. The WK partial
+// sums meet in LDS at the end.
+// ---------------------------------------------------------------------------
+struct GemmParams {
+  const uint16_t* a;
+  const uint8_t* wpk;
+  const uint8_t* spk;
+  uint16_t* c;
+  float* ws;
+  const int32_t* sorted_ids;
+  const int32_t* expert_ids;
+  const int32_t* ntp;
+  const float* topk_w;
+  const int32_t* m_indices;
+  const int32_t* masked_m;
+  uint32_t a_bytes;
+  int32_t mode, a_row_div, num_tiles, nblocks, split, num_slots;
+  int32_t Mb, tiles_per_expert, rows_cap, cap;
+  int32_t E, N, K, NT, KC, BM;
+};
+
+struct RowInfo {
+  bool valid;
+  int32_t a_row;
+  int32_t out_row;
+};
+
+// The tile's expert, or -1 for a tile with no work.
+__device__ __forceinline__ int tile_expert(const GemmParams& p, int tile) {
+  if (p.mode == 0) {
+    if (tile * p.BM >= *p.ntp) return -1;
+    const int e = p.expert_ids[tile];
+    return (e >= 0 && e < p.E) ? e : -1;
+  }
+  if (p.mode == 1) {
+    const int e = p.m_indices[tile * p.BM];
+    return (e >= 0 && e < p.E) ? e : -1;
+  }
+  const int e = tile / p.tiles_per_expert;
+  const int jt = tile - e * p.tiles_per_expert;
+  const int mm = min(max(p.masked_m[e], 0), p.Mb);
+  return (jt * p.BM < mm) ? e : -1;
+}
+
+// Row r of a tile: whether it holds a token, its activation row and its
+// output row.
+__device__ __forceinline__ RowInfo row_info(const GemmParams& p, int tile, int e, int r) {
+  RowInfo ri{false, 0, 0};
+  if (p.mode == 0) {
+    const int pos = tile * p.BM + r;
+    const int s = (pos < p.cap) ? p.sorted_ids[pos] : -1;
+    if (s >= 0 && s < p.num_slots) {
+      ri.valid = true;
+      ri.a_row = s / p.a_row_div;
+      ri.out_row = s;
+    }
+  } else if (p.mode == 1) {
+    const int row = tile * p.BM + r;
+    if (p.m_indices[row] == e) {
+      ri.valid = true;
+      ri.a_row = row;
+      ri.out_row = row;
+    }
+  } else {
+    const int jt = tile - e * p.tiles_per_expert;
+    const int mm = min(max(p.masked_m[e], 0), p.Mb);
+    const int rr = jt * p.BM + r;
+    if (rr < mm) {
+      ri.valid = true;
+      ri.a_row = e * p.Mb + rr;
+      ri.out_row = ri.a_row;
+    }
+  }
+  return ri;
+}
+
+__device__ __forceinline__ u32x4 unpack_128q(uint32_t w) {
+  u32x4 r;
+  r.x = (w & 0x000F000Fu) | 0x43004300u;
+  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
+  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
+  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  return r;
+}
+
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+constexpr int kBufWord3 = 0x00020000;  // raw 32-bit buffer resource, gfx9 family
+constexpr int kNonTemporal = 2;        // streaming load: weights are read once
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kBufWord3);
+}
+
+// Decode the XCD-aware workgroup order. Workgroup i runs on XCD i % 8, and
+// XCD x takes token tiles x, x+8, ... with all of their (column block,
+// split) pieces. A tile's activations then stay in one XCD's L2, and empty
+// tiles spread evenly over the XCDs.
+__device__ __forceinline__ bool decode_bid(const GemmParams& p, int& tile, int& nb, int& sp) {
+  const int bid = blockIdx.x;
+  const int xcd = bid & 7;
+  const int idx = bid >> 3;
+  const int per_tile = p.nblocks * p.split;
+  const int j = idx / per_tile;
+  const int rem = idx - j * per_tile;
+  tile = xcd + 8 * j;
+  nb = rem / p.split;
+  sp = rem - nb * p.split;
+  return tile < p.num_tiles;
+}
+
+template <int TM, int NTW, int WK, int D>
+__global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p) {
+  constexpr int WN = 4 / WK;
+  constexpr int NACC = NTW * TM * 4;
+  __shared__ float s_red[WK > 1 ? 4 * NACC * 64 : 1];
+
+  int tile, nb, sp;
+  if (!decode_bid(p, tile, nb, sp)) return;
+  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
+  if (e < 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int wk = w % WK, wn = w / WK;
+  const int col = lane & 15, kb = lane >> 4;
+
+  const int cs0 = (int)(((int64_t)sp * p.KC) / p.split);
+  const int cs1 = (int)(((int64_t)(sp + 1) * p.KC) / p.split);
+  const int c_begin = cs0 + ((cs1 - cs0) * wk) / WK;
+  const int c_end = cs0 + ((cs1 - cs0) * (wk + 1)) / WK;
+
+  const int nt0 = (nb * WN + wn) * NTW;  // first 16-column tile of this wave
+  const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, NTW * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * p.KC * kSBlockBytes,
+                NTW * p.KC * kSBlockBytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  const uint32_t voff_w = lane * 16;
+  const uint32_t voff_s = col * 8;
+  uint32_t voff_x[TM];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const RowInfo ri = row_info(p, tile, e, tm * 16 + col);
+    voff_x[tm] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
+  }
+
+  struct Stage {
+    u32x4 w[NTW];
+    u32x2 s[NTW];
+    u32x4 x[TM][4];
+  };
+  Stage st[D];
+
+  auto load = [&](Stage& s, int c) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, nt * tile_bytes + c * kWBlockBytes,
+                                                      kNonTemporal);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, (nt * p.KC + c) * kSBlockBytes, 0);
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        s.x[tm][g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x[tm] + g * 64, c * 256, 0);
+  };
+
+  f32x4 acc[NTW][TM];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](const Stage& s) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 xs[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) xs[tm] = mfma16(s.x[tm][g], neg136, zero4);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t wq = s.w[nt][g];
+        const u32x4 wb = unpack_128q(wq);
+        const uint32_t sw = s.s[nt][g >> 1];
+        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const f32x4 pr = mfma16(s.x[tm][g], wb, xs[tm]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][tm][r] = __builtin_fmaf(scv, pr[r], acc[nt][tm][r]);
+        }
+      }
+    }
+  };
+
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (c_begin + d < c_end) load(st[d], c_begin + d);
+  for (int c = c_begin; c < c_end; c += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (c + d < c_end) {
+        compute(st[d]);
+        if (c + d + D < c_end) load(st[d], c + d + D);
+      }
+    }
+  }
+
+  // Output: lane holds rows (tokens) tm*16 + 4*kb + r of column col.
+  auto store = [&](int nt, int tm, int r, float v) {
+    const RowInfo ri = row_info(p, tile, e, tm * 16 + kb * 4 + r);
+    if (!ri.valid) return;
+    const int n = (nt0 + nt) * 16 + col;
+    if (p.split > 1) {
+      p.ws[((size_t)sp * p.rows_cap + ri.out_row) * p.N + n] = v;
+    } else {
+      const float t = (p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+      p.c[(size_t)ri.out_row * p.N + n] = (uint16_t)(pack_bf16x2(v * t, 0.f) & 0xFFFFu);
+    }
+  };
+
+  if constexpr (WK == 1) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) store(nt, tm, r, acc[nt][tm][r]);
+  } else {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          s_red[(w * NACC + (nt * TM + tm) * 4 + r) * 64 + lane] = acc[nt][tm][r];
+    __syncthreads();
+    // wave (wk, wn) finishes tiles nt = wk, wk + WK, ... of its column group
+    for (int nt = wk; nt < NTW; nt += WK) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int i = (nt * TM + tm) * 4 + r;
+          float v = 0.f;
+#pragma unroll
+          for (int j = 0; j < WK; ++j) v += s_red[((wn * WK + j) * NACC + i) * 64 + lane];
+          store(nt, tm, r, v);
+        }
+    }
+  }
+}
+
+// Split-K reduction: c[row] = bf16( sum_s ws[s][row] (* topk weight) ), the
+// splits summed in order ([release] indexed techniques: the split/reduce
+// that the stream-K gate avoids on saturated grids). One thread per
+// (row position, 4 columns).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
+  const int64_t per_row = p.N / 4;
+  const int64_t total = (int64_t)p.num_tiles * p.BM * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int pos = (int)(i / per_row);
+    const int n0 = (int)(i - (int64_t)pos * per_row) * 4;
+    const int tile = pos / p.BM;
+    const int e = tile_expert(p, tile);
+    if (e < 0) continue;
+    const RowInfo ri = row_info(p, tile, e, pos - tile * p.BM);
+    if (!ri.valid) continue;
+    float4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < p.split; ++k) {
+      const float4 v = *(const float4*)(p.ws + ((size_t)k * p.rows_cap + ri.out_row) * p.N + n0);
+      s.x += v.x;
+      s.y += v.y;
+      s.z += v.z;
+      s.w += v.w;
+    }
+    const float t = (p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+    u32x2 o;
+    o.x = pack_bf16x2(s.x * t, s.y * t);
+    o.y = pack_bf16x2(s.z * t, s.w * t);
+    *(u32x2*)(p.c + (size_t)ri.out_row * p.N + n0) = o;
+  }
+}
+
+template <int TM, int NTW, int WK, int D>
+static int launch_small_m_inst(const GemmParams& gp, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_small_m_kernel<TM, NTW, WK, D>), dim3(grid), dim3(256), 0, st, gp);
+  return (int)hipGetLastError();
+}
+
+template <int TM, int NTW, int WK>
+static int launch_small_m_depth(const GemmParams& gp, unsigned grid, hipStream_t st, int depth) {
+  constexpr int D0 = small_m_depth(TM, NTW);
+  if constexpr (TM == 1 && NTW == 4) {
+    if (depth == 2) return launch_small_m_inst<TM, NTW, WK, 2>(gp, grid, st);
+    if (depth == 3) return launch_small_m_inst<TM, NTW, WK, 3>(gp, grid, st);
+    if (depth == 4) return launch_small_m_inst<TM, NTW, WK, 4>(gp, grid, st);
+  }
+  return launch_small_m_inst<TM, NTW, WK, D0>(gp, grid, st);
+}
+
+template <int TM, int NTW>
+static int launch_small_m_wk(const GemmParams& gp, unsigned grid, hipStream_t st, int wk,
+                             int depth) {
+  if (wk == 1) return launch_small_m_depth<TM, NTW, 1>(gp, grid, st, depth);
+  if (wk == 2) return launch_small_m_depth<TM, NTW, 2>(gp, grid, st, depth);
+  if (wk == 4) return launch_small_m_depth<TM, NTW, 4>(gp, grid, st, depth);
+  return (int)hipErrorInvalidConfiguration;
+}
+
+int launch_gemm(const GemmArgs& g, void* stream) {
+  const Layer& L = *g.layer;
+  const qma_plan_t& pl = *g.plan;
+  hipStream_t st = (hipStream_t)stream;
+  GemmParams gp{};
+  gp.a = g.a;
+  gp.wpk = (const uint8_t*)g.packed;
+  gp.spk = (const uint8_t*)g.packed + L.w_bytes;
+  gp.c = g.c;
+  gp.ws = (float*)g.ws;
+  gp.sorted_ids = g.sorted_ids;
+  gp.expert_ids = g.expert_ids;
+  gp.ntp = g.ntp;
+  gp.topk_w = g.topk_weights;
+  gp.m_indices = g.m_indices;
+  gp.masked_m = g.masked_m;
+  gp.a_bytes = (uint32_t)g.a_bytes;
+  gp.mode = g.mode;
+  gp.a_row_div = g.a_row_div;
+  gp.num_tiles = g.num_tiles;
+  gp.nblocks = L.N / pl.block_n;
+  gp.split = pl.split_k;
+  gp.num_slots = g.num_slots;
+  gp.Mb = g.Mb;
+  gp.tiles_per_expert = g.tiles_per_expert;
+  gp.rows_cap = g.rows_cap;
+  gp.cap = g.sorted_cap;
+  gp.E = L.E;
+  gp.N = L.N;
+  gp.K = L.K;
+  gp.NT = (int32_t)L.n_tiles;
+  gp.KC = (int32_t)L.k_chunks;
+  gp.BM = pl.block_m;
+  const int64_t tiles_pad = (g.num_tiles + 7) / 8 * 8;
+  const int64_t grid = tiles_pad * gp.nblocks * gp.split;
+  if (grid <= 0) return 0;
+  if (grid >= (1ll << 24)) return (int)hipErrorInvalidConfiguration;
+  const int tm = pl.block_m / 16;
+  const int wk = pl.waves_k;
+  const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
+  const int depth = pl.k_depth / kChunkK;
+  if (!small_m_supported(tm, ntw) || (wk != 1 && wk != 2 && wk != 4) ||
+      ntw * 16 * (4 / wk) != pl.block_n)
+    return (int)hipErrorInvalidConfiguration;
+  int err = (int)hipErrorInvalidConfiguration;
+#define QMA_SMALL_M_CASE(TM_, NTW_) \
+  if (tm == TM_ && ntw == NTW_) err = launch_small_m_wk<TM_, NTW_>(gp, (unsigned)grid, st, wk, depth);
+  QMA_SMALL_M_CASE(1, 1)
+  QMA_SMALL_M_CASE(1, 2)
+  QMA_SMALL_M_CASE(1, 4)
+  QMA_SMALL_M_CASE(2, 1)
+  QMA_SMALL_M_CASE(2, 2)
+  QMA_SMALL_M_CASE(2, 4)
+  QMA_SMALL_M_CASE(4, 1)
+  QMA_SMALL_M_CASE(4, 2)
+#undef QMA_SMALL_M_CASE
+  if (err != 0) return err;
+  if (gp.split > 1) {
+    const int64_t total = (int64_t)gp.num_tiles * gp.BM * (gp.N / 4);
+    const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+    hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rb), dim3(256), 0, st, gp);
+    err = (int)hipGetLastError();
+  }
+  return err;
+}
+
+// ---------------------------------------------------------------------------
+// silu_and_mul: y[r, j] = silu(x[r, j]) * x[r, I + j] in fp32 ([announce]
+// measurement section: the activation between gate/up and down).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  // silu(g) = g * sigmoid(g). For g >= 0: g / (1 + e^-g). For g < 0, e^-g
+  // overflows fp32 below -88.7 while silu(g) is still a normal number, so
+  // e^g is taken in two halves h = e^(g/2): silu(g) = ((g h) h) / (1 + h h),
+  // with no intermediate overflow or premature underflow.
+  if (g >= 0.0f) return g / (1.0f + __expf(-g)) * u;
+  const float h = __expf(0.5f * g);
+  return ((g * h) * h) / (1.0f + h * h) * u;
+}
+
+__global__ __launch_bounds__(256) void silu_mul_vec8_kernel(const uint16_t* __restrict__ x,
+                                                            uint16_t* __restrict__ y, int64_t R,
+                                                            int32_t I) {
+  const int64_t per_row = I / 8;
+  const int64_t total = R * per_row;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / per_row;
+    const int64_t j = (i - r * per_row) * 8;
+    const u32x4 g = *(const u32x4*)(x + r * 2 * I + j);
+    const u32x4 u = *(const u32x4*)(x + r * 2 * I + I + j);
+    u32x4 o;
+    o.x = pack_bf16x2(silu_mul(bf16_lo(g.x), bf16_lo(u.x)), silu_mul(bf16_hi(g.x), bf16_hi(u.x)));
+    o.y = pack_bf16x2(silu_mul(bf16_lo(g.y), bf16_lo(u.y)), silu_mul(bf16_hi(g.y), bf16_hi(u.y)));
+    o.z = pack_bf16x2(silu_mul(bf16_lo(g.z), bf16_lo(u.z)), silu_mul(bf16_hi(g.z), bf16_hi(u.z)));
+    o.w = pack_bf16x2(silu_mul(bf16_lo(g.w), bf16_lo(u.w)), silu_mul(bf16_hi(g.w), bf16_hi(u.w)));
+    *(u32x4*)(y + r * I + j) = o;
+  }
+}
+
+__global__ __launch_bounds__(256) void silu_mul_scalar_kernel(const uint16_t* __restrict__ x,
+                                                              uint16_t* __restrict__ y, int64_t R,
+                                                              int32_t I) {
+  const int64_t total = R * I;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = i / I;
+    const int64_t j = i - r * I;
+    const float g = __uint_as_float((uint32_t)x[r * 2 * I + j] << 16);
+    const float u = __uint_as_float((uint32_t)x[r * 2 * I + I + j] << 16);
+    y[i] = (uint16_t)(pack_bf16x2(silu_mul(g, u), 0.f) & 0xFFFFu);
+  }
+}
+
+int launch_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I, void* stream) {
+  const bool vec = (I % 8 == 0) && ((uintptr_t)x % 16 == 0) && ((uintptr_t)y % 16 == 0);
+  const int64_t work = vec ? R * (I / 8) : R * I;
+  const unsigned blocks = (unsigned)std::min<int64_t>((work + 255) / 256, 16384);
+  if (vec)
+    hipLaunchKernelGGL(silu_mul_vec8_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, x,
+                       y, R, I);
+  else
+    hipLaunchKernelGGL(silu_mul_scalar_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream,
+                       x, y, R, I);
+  return (int)hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Top-k combine: out[t, n] = sum_k w[t, k] * c2[t*topk + k, n], fp32 sums in
+// k order, slots of experts outside [0, E) skipped when ids are given.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ c2,
+                                                      const float* __restrict__ w,
+                                                      const int32_t* __restrict__ ids,
+                                                      int32_t E, int32_t T, int32_t topk,
+                                                      int32_t N, uint16_t* __restrict__ out) {
+  const int64_t total = (int64_t)T * N;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / N;
+    const int64_t n = i - t * N;
+    float s = 0.f;
+    for (int k = 0; k < topk; ++k) {
+      const int64_t slot = t * topk + k;
+      if (ids && (unsigned)ids[slot] >= (unsigned)E) continue;
+      s = __builtin_fmaf(w[slot], __uint_as_float((uint32_t)c2[slot * N + n] << 16), s);
+    }
+    out[i] = (uint16_t)(pack_bf16x2(s, 0.f) & 0xFFFFu);
+  }
+}
+
+int launch_combine(const uint16_t* c2, const float* w, const int32_t* ids, int32_t E, int32_t T,
+                   int32_t topk, int32_t N, uint16_t* out, void* stream) {
+  const int64_t total = (int64_t)T * N;
+  const unsigned blocks = (unsigned)std::min<int64_t>((total + 255) / 256, 16384);
+  hipLaunchKernelGGL(combine_kernel, dim3(blocks), dim3(256), 0, (hipStream_t)stream, c2, w,
+                     ids, E, T, topk, N, out);
+  return (int)hipGetLastError();
+}
+
+}  // namespace qma

@@ -1,0 +1,114 @@
+"""moe_align on the GPU: routing buffers bit-exact against the oracle over the
+whole capacity, for every workload's routing and fuzzed shapes; the
+validator accepts them and rejects corrupted ones."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import qma_oracle as O
+from quantized_moe_align_amd import inputs, qma
+from quantized_moe_align_amd.moe import to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def run_align(ids, E, B, extra=0, junk=0x7A7A7A7A):
+    T, topk = ids.shape
+    cap, _ = qma.qma_align_sizes(T, topk, E, B)
+    cap += extra
+    blocks = -(-cap // B)
+    s = torch.full((cap,), junk - (1 << 32) if junk >= 1 << 31 else junk, dtype=torch.int32,
+                   device="cuda")
+    e = torch.full((blocks,), junk, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -5, dtype=torch.int32, device="cuda")
+    d_ids = to_device(ids.astype(np.int32)) if ids.size else torch.empty(0, dtype=torch.int32,
+                                                                           device="cuda")
+    qma.qma_moe_align(d_ids if ids.size else None, T, topk, E, B, s, e, n, cap)
+    torch.cuda.synchronize()
+    return d_ids, s, e, n, cap
+
+
+def check(ids, E, B, extra=0):
+    d_ids, s, e, n, cap = run_align(ids, E, B, extra)
+    rs, re_, rn = O.moe_align_fast(ids, E, B, cap)
+    assert int(n.item()) == int(rn)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(e.cpu().numpy(), re_)
+    if ids.size:
+        qma.qma_validate_routing(d_ids, ids.shape[0], ids.shape[1], E, B, s, e, n, cap)
+    return d_ids, s, e, n, cap
+
+
+@pytest.mark.parametrize("name,B", [("tiny", 16), ("tiny", 32), ("ep8_decode", 16),
+                                    ("tp8", 16), ("ep8_prefill", 64), ("ep8_prefill", 128),
+                                    ("ep32_decode", 16), ("ep8_prefill_span", 128)])
+def test_workload_routing_bit_exact(gpu, name, B):
+    wl = inputs.make(name, seed=0, weights=False)
+    check(wl["topk_ids"], wl.E, B, extra=3 * B + 5)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_fuzz_bit_exact(gpu, seed):
+    rng = np.random.default_rng(100 + seed)
+    T = int(rng.integers(1, 3000))
+    topk = int(rng.integers(1, 9))
+    E = int(rng.choice([1, 2, 3, 7, 48, 129, 384, 1024]))
+    B = int(rng.choice([1, 2, 16, 32, 48, 64, 128, 256]))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    if seed % 3 == 0:                      # heavy skew onto one expert
+        ids[rng.random((T, topk)) < 0.7] = E - 1
+    check(ids, E, B, extra=int(rng.integers(0, 2 * B)))
+
+
+def test_edge_cases(gpu):
+    check(np.zeros((1, 1), np.int32), 1, 16)                     # one slot
+    check(np.full((5, 2), -1, np.int32), 4, 16)                  # nothing on this rank
+    check(np.zeros((0, 2), np.int32), 4, 16)                     # no tokens
+    check(np.arange(1024, dtype=np.int32)[:, None], 1024, 16)    # one slot per expert, max E
+    check(np.full((4096, 8), 7, np.int32), 8, 128)               # all on one expert
+    check(np.random.default_rng(0).integers(0, 384, (65536, 1)).astype(np.int32), 384, 64)
+
+
+def test_validator_rejects_corruptions(gpu):
+    wl = inputs.make("tiny", seed=5, weights=False)
+    ids = wl["topk_ids"]
+    d_ids, s, e, n, cap = check(ids, wl.E, 16)
+    T, topk = ids.shape
+
+    def expect_bad(s2=None, e2=None, n2=None, ids2=None):
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_validate_routing(d_ids if ids2 is None else ids2, T, topk, wl.E, 16,
+                                     s if s2 is None else s2, e if e2 is None else e2,
+                                     n if n2 is None else n2, cap)
+        assert ei.value.status == qma.QMA_ERR_ROUTING
+        return ei.value.detail
+
+    sh = s.cpu().numpy()
+    R = T * topk
+    p = next(i for i in range(16, int(n.item())) if sh[i] < R)  # a slot of a later block
+    s2 = s.clone(); s2[0] = int(sh[p])                           # wrong block and twice
+    d = expect_bad(s2=s2)
+    assert "placed" in d or "twice" in d
+    s3 = s.clone(); s3[1] = s3[0]                                # duplicate
+    expect_bad(s2=s3)
+    e2 = e.clone(); e2[0] = wl.E                                 # expert out of range
+    expect_bad(e2=e2)
+    n2 = n.clone(); n2[0] = n[0] + 1                             # not a block multiple
+    expect_bad(n2=n2)
+    n3 = n.clone(); n3[0] = n[0] - 16                            # drops a block
+    expect_bad(n2=n3)
+    ids2 = d_ids.clone(); ids2[0, 0] = wl.E + 3                  # id outside [-1, E)
+    expect_bad(ids2=ids2)
+
+
+def test_validate_contiguous(gpu):
+    good = inputs.make_contiguous("c", 0, 3, 0, 64, 32, counts=[5, 0, 130], weights=False)
+    m = to_device(good["m_indices"])
+    qma.qma_validate_contiguous(m, m.numel(), 3)
+    bad = m.clone(); bad[10] = 0                                 # id after padding
+    with pytest.raises(qma.QmaError) as ei:
+        qma.qma_validate_contiguous(bad, m.numel(), 3)
+    assert ei.value.status == qma.QMA_ERR_ROUTING
+    bad2 = m.clone(); bad2[129] = 1                              # two experts in a block
+    with pytest.raises(qma.QmaError):
+        qma.qma_validate_contiguous(bad2, m.numel(), 3)

@@ -1,0 +1,341 @@
+"""Expert GEMMs on the GPU against the oracle, at sizes the oracle finishes in
+seconds (several tiles, ragged tails, every kernel instance), through the C
+ABI: random inputs within the per-expert tolerance, integer-exact inputs
+bit-for-bit, and the method's invariants and edge cases."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import qma_oracle as O
+from quantized_moe_align_amd import inputs, qma
+from quantized_moe_align_amd.moe import (ExpertWeights, IndexedMoE, empty_bf16, to_device,
+                                         to_host, workspace_for)
+from gpu_common import assert_per_expert, bf16_pow2, bf16_small_ints, rne, slot_experts
+
+pytestmark = pytest.mark.gpu
+
+SENT = 0x5A5A  # pattern pre-filled into outputs to detect untouched rows
+
+
+def weights(rng, E, N, K, integer=False):
+    w = inputs.random_words(rng, (E, N, K // 8))
+    s = bf16_pow2(rng, (E, N, K // 32)) if integer else \
+        inputs.bf16_normal(rng, (E, N, K // 32), 0.02, absolute=True)
+    return w, s
+
+
+def indexed(a_bits, a_row_div, ids, w, s, *, T=None, topk=None, force_bm=0, override=None,
+            extra_cap=0, junk_tail=False, topk_w=None, pre=None):
+    """Run moe_align + one indexed GEMM through the ABI; return output bits."""
+    E, N, K8 = w.shape
+    ids = np.asarray(ids, np.int32)
+    T = ids.shape[0] if T is None else T
+    topk = ids.shape[1] if topk is None else topk
+    R = T * topk
+    W = ExpertWeights(w, s)
+    plan = qma.qma_plan_indexed(W.layer, T, topk, force_bm)
+    for k, v in (override or {}).items():
+        setattr(plan, k, v)
+    B = plan.block_m
+    cap = qma.qma_align_sizes(T, topk, E, B)[0] + extra_cap
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    expert_ids = torch.empty(-(-cap // B), dtype=torch.int32, device="cuda")
+    ntp = torch.empty(1, dtype=torch.int32, device="cuda")
+    d_ids = to_device(ids)
+    qma.qma_moe_align(d_ids, T, topk, E, B, sorted_ids, expert_ids, ntp, cap)
+    if junk_tail:
+        torch.cuda.synchronize()
+        n = int(ntp.item())
+        sorted_ids[n:] = 0                 # looks like a real slot
+        expert_ids[n // B:] = E - 1        # looks like a real expert
+    a = to_device(a_bits)
+    c = torch.full((R, N), SENT, dtype=torch.int16, device="cuda") if pre is None else pre
+    ws = workspace_for(plan)
+    tw = None if topk_w is None else torch.from_numpy(np.ascontiguousarray(topk_w, np.float32)).cuda()
+    qma.qma_indexed_gemm(W.layer, plan, a, a_bits.shape[0], a_row_div, W.packed, sorted_ids,
+                         expert_ids, ntp, cap, R, tw, c, ws, 0 if ws is None else ws.numel())
+    torch.cuda.synchronize()
+    return to_host(c, bf16=True), plan
+
+
+SHAPES = [  # (E, T, topk, K, N)
+    (8, 64, 2, 256, 256),        # tiny gate_up
+    (8, 128, 1, 128, 256),       # tiny down (K = I = 128, one chunk)
+    (6, 100, 3, 512, 384),       # ragged: N % 128 != 0, tails in every expert
+    (5, 37, 4, 1024, 160),       # 16-wide column tail (N = 10 tiles)
+]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("force_bm", [0, 16, 32, 64])
+def test_indexed_random_within_tolerance(gpu, shape, force_bm):
+    E, T, topk, K, N = shape
+    rng = np.random.default_rng(hash((shape, force_bm)) % 2**32)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=force_bm)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    assert_per_expert(got, ref, slot_experts(ids, E), f"{shape} bm={plan.block_m}")
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("force_bm,ntw,wk", [(0, 0, 0), (16, 1, 4), (16, 2, 1), (16, 4, 2),
+                                             (16, 4, 4), (16, 4, 1), (32, 4, 4), (32, 2, 2),
+                                             (32, 1, 1), (64, 2, 4), (64, 1, 2)])
+def test_indexed_integer_exact_bitwise(gpu, shape, force_bm, ntw, wk):
+    E, T, topk, K, N = shape
+    block_n = ntw * 16 * (4 // wk) if ntw else 0
+    if block_n and N % block_n:
+        pytest.skip("width does not divide N")
+    rng = np.random.default_rng(7 + E + T)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    got, _ = indexed(a, topk, ids, w, s, force_bm=force_bm,
+                     override={"block_n": block_n, "waves_k": wk, "split_k": 1}
+                     if block_n else None)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(got[valid], rne(ref[valid]))
+    assert np.all(got[~valid] == SENT)           # rows of slots not on this rank untouched
+
+
+@pytest.mark.parametrize("split", [2, 3, 4])
+def test_split_k_matches_unsplit(gpu, split):
+    E, T, topk, K, N = 3, 40, 2, 2048, 256
+    rng = np.random.default_rng(split)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    base, p0 = indexed(a, topk, ids, w, s)
+    got, p1 = indexed(a, topk, ids, w, s, override={"split_k": split})
+    assert p1.split_k == split and qma.qma_workspace_bytes(p1) > 0
+    assert np.array_equal(base, got)
+    assert np.array_equal(got, rne(O.moe_gemm_by_slot(a, topk, ids, w, s)))
+    # random inputs: same bar as the unsplit kernel
+    w2, s2 = weights(rng, E, N, K)
+    a2 = inputs.bf16_normal(rng, (T, K))
+    got2, _ = indexed(a2, topk, ids, w2, s2, override={"split_k": split})
+    assert_per_expert(got2, O.moe_gemm_by_slot(a2, topk, ids, w2, s2), slot_experts(ids, E))
+
+
+def test_overallocated_buffers_with_junk_tail(gpu):
+    E, T, topk, K, N = 6, 50, 2, 512, 128
+    rng = np.random.default_rng(11)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    base, _ = indexed(a, topk, ids, w, s)
+    got, _ = indexed(a, topk, ids, w, s, extra_cap=200, junk_tail=True)
+    assert np.array_equal(base, got)
+
+
+def test_identity_weights_gather_exactly(gpu):
+    # W = [I | 0]: the GEMM is a pure gather. With integer activations every
+    # sum is exact, so the output equals the gathered rows bit for bit; with
+    # random activations it is within the tolerance (the zero-point fold
+    # sums x*(128+q) and -136*x in fp32).
+    E, T, topk, K, N = 4, 30, 3, 256, 128
+    rng = np.random.default_rng(12)
+    q = np.full((E, N, K), 8)
+    for n in range(N):
+        q[:, n, n] = 9
+    w = O.pack_uint4(q)
+    s = np.full((E, N, K // 32), 0x3F80, np.uint16)
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    slots = np.arange(T * topk)
+    a = bf16_small_ints(rng, (T, K), -100, 100)
+    got, _ = indexed(a, topk, ids, w, s)
+    assert np.array_equal(got, a[slots // topk, :N])
+    a2 = inputs.bf16_normal(rng, (T, K))
+    got2, _ = indexed(a2, topk, ids, w, s)
+    assert_per_expert(got2, O.bf16_to_f64(a2[slots // topk, :N]), slot_experts(ids, E))
+
+
+def test_nan_poisoned_unused_data_is_never_read(gpu):
+    E, T, topk, K, N = 8, 40, 2, 256, 128
+    rng = np.random.default_rng(13)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, 5, (T, topk)).astype(np.int32)     # experts 5..7 get no tokens
+    ids[3] = -1                                               # token 3 is not on this rank
+    s_poison = s.copy()
+    s_poison[5:] = 0x7FC0
+    a_poison = a.copy()
+    a_poison[3] = 0x7FC0
+    got, _ = indexed(a_poison, topk, ids, w, s_poison)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    assert_per_expert(got, ref, slot_experts(ids, E))
+
+
+def test_topk_weights_in_epilogue(gpu):
+    E, T, topk, K, N = 4, 20, 2, 256, 128
+    rng = np.random.default_rng(14)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T * topk, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    tw = rng.random(T * topk).astype(np.float32)
+    got, _ = indexed(a, 1, ids, w, s, topk_w=tw)             # down-style: row = slot
+    ref = O.moe_gemm_by_slot(a, 1, ids, w, s, topk_weights=tw)
+    assert_per_expert(got, ref, slot_experts(ids, E))
+
+
+def test_permutation_equivariance_bitwise(gpu):
+    E, T, topk, K, N = 6, 48, 2, 512, 128
+    rng = np.random.default_rng(15)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    perm = rng.permutation(T)
+    base, _ = indexed(a, topk, ids, w, s)
+    got, _ = indexed(a[perm], topk, ids[perm], w, s)
+    slot_perm = (perm[:, None] * topk + np.arange(topk)).reshape(-1)
+    assert np.array_equal(got, base[slot_perm])
+
+
+# ---- grouped paths -------------------------------------------------------
+
+def contiguous(a_bits, m_idx, w, s, override=None):
+    E, N, K8 = w.shape
+    W = ExpertWeights(w, s, qma.PATH_GROUPED_CONTIGUOUS)
+    M = m_idx.size
+    plan = qma.qma_plan_grouped(W.layer, M, 0)
+    for k, v in (override or {}).items():
+        setattr(plan, k, v)
+    c = torch.full((M, N), SENT, dtype=torch.int16, device="cuda")
+    ws = workspace_for(plan)
+    qma.qma_grouped_contiguous_gemm(W.layer, plan, to_device(a_bits), to_device(m_idx), M,
+                                    W.packed, c, ws, 0 if ws is None else ws.numel())
+    torch.cuda.synchronize()
+    return to_host(c, bf16=True)
+
+
+def masked(a_bits, masked_m, expected_m, w, s, override=None):
+    E, N, K8 = w.shape
+    Eb, Mb, K = a_bits.shape
+    W = ExpertWeights(w, s, qma.PATH_GROUPED_MASKED)
+    plan = qma.qma_plan_grouped(W.layer, Mb, expected_m)
+    for k, v in (override or {}).items():
+        setattr(plan, k, v)
+    c = torch.full((E, Mb, N), SENT, dtype=torch.int16, device="cuda")
+    ws = workspace_for(plan)
+    qma.qma_grouped_masked_gemm(W.layer, plan, to_device(a_bits), to_device(masked_m), Mb,
+                                expected_m, W.packed, c, ws, 0 if ws is None else ws.numel())
+    torch.cuda.synchronize()
+    return to_host(c, bf16=True)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_contiguous(gpu, integer):
+    E, K, N = 5, 512, 256
+    rng = np.random.default_rng(20 + integer)
+    wl = inputs.make_contiguous("c", 3, E, 0, K, N // 2, counts=[130, 0, 7, 128, 1],
+                                weights=False)
+    m_idx = wl["m_indices"]
+    w, s = weights(rng, E, N, K, integer)
+    a = bf16_small_ints(rng, (m_idx.size, K)) if integer else wl["a"]
+    a_poison = a.copy()
+    a_poison[m_idx < 0] = 0x7FC0                             # padding rows are never read
+    for override in (None, {"block_m": 16, "block_n": 64, "waves_k": 4},
+                     {"block_m": 32, "block_n": 128, "waves_k": 2}, {"split_k": 2}):
+        got = contiguous(a_poison, m_idx, w, s, override)
+        ref = O.grouped_contiguous(a, m_idx, w, s)
+        valid = m_idx >= 0
+        if integer:
+            assert np.array_equal(got[valid], rne(ref[valid]))
+        else:
+            assert_per_expert(got, np.where(valid[:, None], ref, np.nan), m_idx, "contiguous")
+        assert np.all(got[~valid] == SENT)
+
+
+@pytest.mark.parametrize("integer", [False, True])
+def test_masked(gpu, integer):
+    E, Mb, K, N = 6, 64, 512, 256
+    rng = np.random.default_rng(30 + integer)
+    masked_m = np.array([32, 0, 64, 1, 17, 33], np.int32)
+    w, s = weights(rng, E, N, K, integer)
+    a = bf16_small_ints(rng, (E, Mb, K)) if integer else inputs.bf16_normal(rng, (E, Mb, K))
+    a_poison = a.copy()
+    for e in range(E):
+        a_poison[e, masked_m[e]:] = 0x7FC0                   # rows past masked_m unread
+    for expected in (32, 16, 64):
+        got = masked(a_poison, masked_m, expected, w, s)
+        ref = O.grouped_masked(a, masked_m, w, s)
+        row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
+        valid = row_e >= 0
+        if integer:
+            assert np.array_equal(got[valid], rne(ref[valid]))
+        else:
+            assert_per_expert(got.reshape(E * Mb, N), ref.reshape(E * Mb, N),
+                              row_e.reshape(-1), f"masked expected={expected}")
+        assert np.all(got[~valid] == SENT)
+
+
+def test_indexed_equals_contiguous_on_same_rows(gpu):
+    E, K, N = 4, 512, 128
+    rng = np.random.default_rng(40)
+    counts = [20, 3, 0, 45]
+    wl = inputs.make_contiguous("c", 4, E, 0, K, N // 2, counts=counts, weights=False)
+    m_idx = wl["m_indices"]
+    w, s = weights(rng, E, N, K)
+    got_c = contiguous(wl["a"], m_idx, w, s)
+    ids = np.where(m_idx >= 0, m_idx, -1).astype(np.int32)[:, None]
+    got_i, _ = indexed(wl["a"], 1, ids, w, s)
+    valid = m_idx >= 0
+    assert_per_expert(got_c, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx)
+    np.testing.assert_array_equal(O.bf16_to_f64(got_c[valid]), O.bf16_to_f64(got_i[valid]))
+
+
+# ---- the chained layer and graph capture ---------------------------------
+
+def _tiny_moe(seed=0):
+    wl = inputs.make("tiny", seed=seed)
+    w13 = ExpertWeights(wl["w13"], wl["s13"])
+    w2 = ExpertWeights(wl["w2"], wl["s2"])
+    moe = IndexedMoE(w13, w2, wl.T, wl.topk)
+    return wl, moe
+
+
+def test_tiny_layer_chain(gpu):
+    wl, moe = _tiny_moe()
+    a = to_device(wl["a"])
+    ids = to_device(wl["topk_ids"])
+    moe.forward(a, ids)
+    torch.cuda.synchronize()
+    se = slot_experts(wl["topk_ids"], wl.E)
+    c1 = to_host(moe.c1, bf16=True)
+    h = to_host(moe.h, bf16=True)
+    c2 = to_host(moe.c2, bf16=True)
+    assert_per_expert(c1, O.moe_gemm_by_slot(wl["a"], wl.topk, wl["topk_ids"], wl["w13"],
+                                             wl["s13"]), se, "gate_up")
+    assert_per_expert(c2, O.moe_gemm_by_slot(h, 1, wl["topk_ids"], wl["w2"], wl["s2"]), se,
+                      "down (GPU's own activation as input)")
+    # fully chained: the oracle rounds C1 and H to bf16 where the GPU does
+    c1_ref = rne(O.moe_gemm_by_slot(wl["a"], wl.topk, wl["topk_ids"], wl["w13"], wl["s13"]))
+    h_ref = rne(O.silu_and_mul(c1_ref))
+    assert_per_expert(c2, O.moe_gemm_by_slot(h_ref, 1, wl["topk_ids"], wl["w2"], wl["s2"]),
+                      se, "down (chained)")
+
+
+def test_graph_capture_replays_match_eager(gpu):
+    wl, moe = _tiny_moe(seed=1)
+    a = to_device(wl["a"])
+    ids = to_device(wl["topk_ids"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(a, ids)                      # warm up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = to_host(moe.c2, bf16=True).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(a, ids)
+    for i in range(4):
+        moe.c2.fill_(0)
+        moe.routing.sorted_ids.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"

@@ -1,0 +1,182 @@
+"""The C ABI without a GPU: the library loads, exports every declared
+symbol, rejects bad schemes and shapes at load, and the planner follows its
+rules. No call here reaches a kernel launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_align_amd import qma
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                      "include", "qma.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(qma.LIB_PATH):
+        pytest.skip("libqma.so not built")
+    return qma.lib()
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(qma_[a-z_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_symbols()
+    assert len(names) >= 20
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qma.EXPORTS)
+
+
+def test_version_and_status_strings(L):
+    assert "gfx950" in qma.qma_version()
+    assert qma._status_name(qma.QMA_ERR_UNSUPPORTED) == "QMA_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("field,value", [
+    ("weight_bits", 8), ("zero_point", 0), ("group_size", 64), ("group_size", 128),
+    ("scale_dtype", qma.DTYPE_FP16), ("scale_dtype", qma.DTYPE_FP32),
+    ("act_dtype", qma.DTYPE_FP16), ("pack_format", 2)])
+def test_unsupported_schemes_fail_at_load(L, field, value):
+    with pytest.raises(qma.QmaError) as ei:
+        qma.qma_layer_create(8, 256, 256, qma.PATH_INDEXED, qma.w4a16_desc(**{field: value}))
+    assert ei.value.status == qma.QMA_ERR_UNSUPPORTED
+    assert field.split("_")[0] in ei.value.detail or "only" in ei.value.detail
+
+
+@pytest.mark.parametrize("E,N,K", [(0, 256, 256), (8, 24, 256), (8, 256, 96), (8, 256, 200),
+                                   (8, 0, 256)])
+def test_bad_shapes(L, E, N, K):
+    with pytest.raises(qma.QmaError) as ei:
+        qma.qma_layer_create(E, N, K)
+    assert ei.value.status == qma.QMA_ERR_INVALID_ARG
+
+
+def test_null_out_pointer(L):
+    d = qma.w4a16_desc()
+    assert L.qma_layer_create(ctypes.byref(d), 8, 256, 256, 0, None) == qma.QMA_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("E,N,K,profile", [
+    (48, 4096, 7168, "ep_gate_up"), (48, 7168, 2048, "ep_down"),
+    (384, 512, 7168, "tp_gate_up"), (384, 7168, 256, "tp_down"),
+    (8, 256, 256, "ep_gate_up"), (8, 256, 128, "ep_down")])
+def test_profile_inferred_from_shape(L, E, N, K, profile):
+    lay = qma.qma_layer_create(E, N, K)
+    try:
+        info = qma.qma_layer_info(lay)
+        assert info["profile"] == profile and (info["E"], info["N"], info["K"]) == (E, N, K)
+        # uint4 + one bf16 scale per 32 values = 0.5625 bytes per weight
+        assert qma.qma_packed_weight_bytes(lay) == E * N * K * 9 // 16
+    finally:
+        qma.qma_layer_destroy(lay)
+
+
+def _plan(E, N, K, T, topk, force=0):
+    lay = qma.qma_layer_create(E, N, K)
+    try:
+        return qma.qma_plan_indexed(lay, T, topk, force)
+    finally:
+        qma.qma_layer_destroy(lay)
+
+
+def test_plan_decode_ep8():
+    p = _plan(48, 4096, 7168, 576, 1)
+    assert p.kernel == qma.KERNEL_SMALL_M and p.block_m == 16
+    assert p.block_n == 64 and p.waves_k == 4 and p.split_k == 1  # 48 x 64 tiles
+    assert p.tok_e_x100 == 1200 and p.rows == 576
+    assert qma.qma_workspace_bytes(p) == 0
+
+
+def test_plan_tp8_and_tiny():
+    p = _plan(384, 512, 7168, 256, 8)
+    assert p.block_m == 16 and p.tok_e_x100 == 533 and p.split_k == 1
+    t = _plan(8, 256, 256, 64, 2)
+    assert t.block_m == 16 and t.waves_k == 1          # K = 256: waves split columns
+    assert t.block_n == 128                            # 16 tiles: the narrower width
+    assert t.split_k == 1                              # K = 256: no room to split
+    d = _plan(48, 7168, 2048, 576, 1)                  # EP8 down: K = 2048
+    assert d.waves_k == 2 and d.block_n == 128 and d.split_k == 1
+
+
+def test_block_m_follows_tok_e():
+    for tok_e, bm in [(1, 16), (15, 16), (16, 16), (17, 32), (32, 32), (33, 64), (79, 64)]:
+        assert _plan(48, 4096, 7168, 48 * tok_e, 1).block_m == bm, tok_e
+
+
+def test_split_k_gate_turns_on_only_when_underfilled():
+    # 1 expert: 64 tiles at 64 columns, 128 at 32 < 256 CUs -> split
+    p = _plan(1, 4096, 7168, 12, 1)
+    assert p.block_n == 32 and p.est_tiles == 128 and p.split_k == 2
+    assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
+    # 2 experts: the 32-column width gives exactly 256 tiles -> no split
+    assert _plan(2, 4096, 7168, 24, 1).split_k == 1
+    # EP32 share: 12 experts x 64 tiles = 768 >= 256 -> full width, no split
+    q = _plan(12, 4096, 7168, 144, 1)
+    assert q.split_k == 1 and q.block_n == 64
+
+
+def test_plan_rejects_bad_force_and_wrong_path():
+    with pytest.raises(qma.QmaError):
+        _plan(48, 4096, 7168, 576, 1, force=48)
+    lay = qma.qma_layer_create(8, 256, 256, qma.PATH_GROUPED_MASKED)
+    try:
+        with pytest.raises(qma.QmaError):
+            qma.qma_plan_indexed(lay, 64, 2)
+        p = qma.qma_plan_grouped(lay, 64, 32)
+        assert p.block_m == 32 and p.rows == 8 * 64
+        with pytest.raises(qma.QmaError):
+            qma.qma_plan_grouped(lay, 64, 65)
+    finally:
+        qma.qma_layer_destroy(lay)
+
+
+def test_align_sizes_closed_form():
+    assert qma.qma_align_sizes(64, 2, 8, 16) == (128 + 8 * 15, (128 + 120 + 15) // 16)
+    assert qma.qma_align_sizes(0, 1, 4, 64) == (4 * 63, 4)
+    with pytest.raises(qma.QmaError):
+        qma.qma_align_sizes(-1, 1, 4, 16)
+
+
+def test_host_checks_before_any_launch(L):
+    # every case below must be rejected on the host, before a kernel launch
+    lay = qma.qma_layer_create(8, 256, 256)
+    other = qma.qma_layer_create(8, 512, 256)
+    try:
+        p = qma.qma_plan_indexed(lay, 64, 2)
+        cap = qma.qma_align_sizes(64, 2, 8, p.block_m)[0]
+        fake = 1 << 20                                   # never dereferenced
+        with pytest.raises(qma.QmaError) as e1:           # null c
+            qma.qma_indexed_gemm(lay, p, fake, 64, 2, fake, fake, fake, fake, cap, 128,
+                                 None, None, stream=0)
+        assert e1.value.status == qma.QMA_ERR_INVALID_ARG
+        with pytest.raises(qma.QmaError) as e2:           # plan from another layer
+            qma.qma_indexed_gemm(other, p, fake, 64, 2, fake, fake, fake, fake, cap, 128,
+                                 None, fake, stream=0)
+        assert e2.value.status == qma.QMA_ERR_INVALID_ARG
+        with pytest.raises(qma.QmaError) as e3:           # too few activation rows
+            qma.qma_indexed_gemm(lay, p, fake, 10, 2, fake, fake, fake, fake, cap, 128,
+                                 None, fake, stream=0)
+        assert e3.value.status == qma.QMA_ERR_INVALID_ARG
+        p.split_k = 2                                      # needs a workspace now
+        with pytest.raises(qma.QmaError) as e4:
+            qma.qma_indexed_gemm(lay, p, fake, 64, 2, fake, fake, fake, fake, cap, 128,
+                                 None, fake, None, 0, stream=0)
+        assert e4.value.status == qma.QMA_ERR_WORKSPACE
+        with pytest.raises(qma.QmaError) as e5:           # capacity below the bound
+            qma.qma_moe_align(fake, 64, 2, 8, 16, fake, fake, fake, cap - 1, stream=0)
+        assert e5.value.status == qma.QMA_ERR_INVALID_ARG
+        with pytest.raises(qma.QmaError) as e6:           # too many experts
+            qma.qma_moe_align(fake, 4, 1, 2048, 16, fake, fake, fake, 4 + 2048 * 15, stream=0)
+        assert e6.value.status == qma.QMA_ERR_INVALID_ARG
+        with pytest.raises(qma.QmaError) as e7:           # misaligned packed weights
+            qma.qma_prepack(lay, fake, fake, fake + 4, stream=0)
+        assert e7.value.status == qma.QMA_ERR_INVALID_ARG
+    finally:
+        qma.qma_layer_destroy(lay)
+        qma.qma_layer_destroy(other)
