@@ -108,6 +108,26 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->k_depth = qma::small_m_depth(tm, ntw) * qma::kChunkK;
 }
 
+// Large-M kernel: 128-token tiles, 256 columns per workgroup.
+bool large_m_fits(const Layer& L) { return L.N % 256 == 0; }
+
+void plan_large_m(const Layer& L, int32_t tiles_m, qma_plan_t* p) {
+  p->kernel = QMA_KERNEL_LARGE_M;
+  p->block_m = 128;
+  p->block_n = 256;
+  p->waves_k = 1;
+  p->k_depth = 2 * qma::kChunkK;
+  const int32_t tiles = (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / 256), 1 << 30);
+  p->est_tiles = tiles;
+  int32_t split = 1;
+  if (tiles < qma::kNumCUs) {
+    const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / 4));
+    split = std::min<int32_t>({ceil_div(qma::kNumCUs, std::max(tiles, 1)), max_split, 8});
+    split = std::max<int32_t>(split, 1);
+  }
+  p->split_k = split;
+}
+
 void plan_common(const Layer& L, qma_plan_t* p) {
   std::memset(p, 0, sizeof(*p));
   p->path = L.path;
@@ -138,6 +158,9 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "plan was made for another layer");
   if (plan->kernel != QMA_KERNEL_SMALL_M && plan->kernel != QMA_KERNEL_LARGE_M)
     return fail(QMA_ERR_INVALID_ARG, "plan has unknown kernel %d", plan->kernel);
+  if (plan->kernel == QMA_KERNEL_LARGE_M &&
+      (plan->block_m != 128 || plan->block_n != 256 || L.N % 256 != 0))
+    return fail(QMA_ERR_INVALID_ARG, "large-M plan needs block 128 x 256 and N %% 256 == 0");
   if (plan->block_m < 16 || plan->block_m % 16 != 0 ||
       (plan->kernel == QMA_KERNEL_SMALL_M && plan->block_m > 64))
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
@@ -268,16 +291,24 @@ qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
   out->rows = (int32_t)R;
   const double tok_e = (double)R / L.E;
   out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
-  int32_t bm;
-  if (force_block_m != 0) {
-    if (force_block_m != 16 && force_block_m != 32 && force_block_m != 64)
-      return fail(QMA_ERR_INVALID_ARG, "force_block_m %d not in {16,32,64}", force_block_m);
-    bm = force_block_m;
-  } else {
-    // Below 80 routed rows per expert: the smallest of 16, 32, 64 >= tok_e.
-    bm = tok_e <= 16 ? 16 : (tok_e <= 32 ? 32 : 64);
-  }
   const int64_t e_active = std::min<int64_t>(L.E, std::max<int64_t>(R, 1));
+  if (force_block_m != 0 && force_block_m != 16 && force_block_m != 32 &&
+      force_block_m != 64 && force_block_m != 128)
+    return fail(QMA_ERR_INVALID_ARG, "force_block_m %d not in {16,32,64,128}", force_block_m);
+  if (force_block_m == 128 && !large_m_fits(L))
+    return fail(QMA_ERR_INVALID_ARG, "block_m 128 needs N %% 256 == 0 (N=%d)", L.N);
+  // At or above 80 routed rows per expert the large-M kernel amortises the
+  // dequantisation over 128 tokens; below, the small-M kernel takes the
+  // smallest of 16, 32, 64 rows that covers tok_e.
+  const bool large = force_block_m == 128 ||
+                     (force_block_m == 0 && tok_e >= 80.0 && large_m_fits(L));
+  if (large) {
+    const int64_t per_e = std::max<int64_t>(1, ceil_div((int64_t)std::ceil(tok_e), 128));
+    plan_large_m(L, (int32_t)std::min<int64_t>(e_active * per_e, 1 << 30), out);
+    return ok();
+  }
+  const int32_t bm = force_block_m != 0 ? force_block_m
+                                        : (tok_e <= 16 ? 16 : (tok_e <= 32 ? 32 : 64));
   const int64_t per_e = std::max<int64_t>(1, ceil_div((int64_t)std::ceil(tok_e), bm));
   plan_small_m(L, bm, (int32_t)std::min<int64_t>(e_active * per_e, 1 << 30), out);
   return ok();
@@ -295,7 +326,10 @@ qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
     out->rows = M;
     const double tok_e = (double)M / L.E;
     out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
-    plan_small_m(L, 64, std::max(1, M / 64), out);
+    if (tok_e >= 80.0 && large_m_fits(L))
+      plan_large_m(L, std::max(1, M / 128), out);
+    else
+      plan_small_m(L, 64, std::max(1, M / 64), out);
     return ok();
   }
   if (L.path == QMA_PATH_GROUPED_MASKED) {

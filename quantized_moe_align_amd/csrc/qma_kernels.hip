@@ -446,10 +446,36 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
     }
   };
 
+  // K loop with D chunks in flight. Waves with at least 2*D chunks run a
+  // main loop whose loads are unconditional, so the wait counts before each
+  // use allow every later chunk's loads to stay in flight; only the final
+  // drain (and short ranges) take the guarded path.
+  int c = c_begin;
+  if (c_end - c_begin >= 2 * D) {
 #pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (c_begin + d < c_end) load(st[d], c_begin + d);
-  for (int c = c_begin; c < c_end; c += D) {
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      load(st[d], c + d);
+    }
+    for (; c + 2 * D <= c_end; c += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        // The barriers keep each stage's loads in issue order behind its
+        // compute; without them the scheduler sinks loads of one stage past
+        // the next stage's compute and the wait counts serialise the stages.
+        __builtin_amdgcn_sched_barrier(0);
+        compute(st[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        load(st[d], c + D + d);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (c + d < c_end) load(st[d], c + d);
+  }
+  for (; c < c_end; c += D) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (c + d < c_end) {
@@ -536,6 +562,201 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M expert GEMM (prefill shapes: 128-token tiles).
+//
+// Workgroup: 4 waves over one 128-token tile and 256 weight columns, each
+// wave owning 64 columns (4 tiles of 16) for all 128 tokens (8 tiles of 16).
+// The token tile is staged in LDS in 128-wide K chunks: each wave copies 32
+// rows with 16-byte direct-to-LDS buffer loads (rows the tile does not use
+// get an out-of-range offset and arrive as zeros without being read). Slot j
+// of LDS row r holds the row's 16-byte segment j ^ (r % 16), so the 16 rows
+// an MFMA operand read touches fall in distinct banks. Three LDS buffers
+// give two chunks of prefetch with one barrier per chunk.
+//
+// Weights never pass through LDS. Each wave loads its packed fragments
+// directly: one 32-bit word per lane per 16x32 MFMA tile. It dequantises
+// them in registers to bf16((q - 8) * scale), using exact fp32 (q * s - 8 s
+// is one rounding of an exact 12-bit product) and one round to bf16. That
+// work is paid once per 128 tokens. This is the MFMA-bound regime, where
+// the small-M kernel's per-output scale fold would cost more VALU than the
+// MFMAs themselves.
+// ---------------------------------------------------------------------------
+constexpr int kLmBM = 128;          // tokens per tile
+constexpr int kLmBN = 256;          // columns per workgroup
+constexpr int kLmRowBytes = 256;    // one 128-wide K chunk of a bf16 row
+constexpr int kLmBufBytes = kLmBM * kLmRowBytes;
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// Eight uint4 values of one packed word (nibble order k0 k2 k4 k6 k1 k3 k5 k7)
+// -> eight bf16 (q - 8) * s in k order, as an MFMA operand.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes: k0 k4 k1 k5
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes: k2 k6 k3 k7
+  const float k0 = __builtin_fmaf((float)(lo & 0xFFu), s, neg8s);
+  const float k4 = __builtin_fmaf((float)((lo >> 8) & 0xFFu), s, neg8s);
+  const float k1 = __builtin_fmaf((float)((lo >> 16) & 0xFFu), s, neg8s);
+  const float k5 = __builtin_fmaf((float)(lo >> 24), s, neg8s);
+  const float k2 = __builtin_fmaf((float)(hi & 0xFFu), s, neg8s);
+  const float k6 = __builtin_fmaf((float)((hi >> 8) & 0xFFu), s, neg8s);
+  const float k3 = __builtin_fmaf((float)((hi >> 16) & 0xFFu), s, neg8s);
+  const float k7 = __builtin_fmaf((float)(hi >> 24), s, neg8s);
+  return u32x4{cvt_pk_bf16(k0, k1), cvt_pk_bf16(k2, k3), cvt_pk_bf16(k4, k5),
+               cvt_pk_bf16(k6, k7)};
+}
+
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p) {
+  constexpr int NTW = 4, MT = 8;
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[3][kLmBufBytes];
+  __shared__ int32_t s_arow[kLmBM];
+  __shared__ int32_t s_out[kLmBM];
+
+  int tile, nb, sp;
+  if (!decode_bid(p, tile, nb, sp)) return;
+  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
+  if (e < 0) return;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int col = lane & 15, kb = lane >> 4;
+
+  if (threadIdx.x < kLmBM) {
+    const RowInfo ri = row_info(p, tile, e, threadIdx.x);
+    s_arow[threadIdx.x] = ri.valid ? ri.a_row : -1;
+    s_out[threadIdx.x] = ri.valid ? ri.out_row : -1;
+  }
+  __syncthreads();
+
+  const int c0 = (int)(((int64_t)sp * p.KC) / p.split);
+  const int c1 = (int)(((int64_t)(sp + 1) * p.KC) / p.split);
+  const int n = c1 - c0;
+
+  // token rows: wave w copies rows 32w .. 32w+31, four per instruction
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  uint32_t voff_a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int row = 32 * w + 4 * i + kb;
+    const int ar = s_arow[row];
+    const uint32_t seg = (uint32_t)(col ^ (row & 15));
+    voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
+  }
+  auto load_a = [&](int buf, int c) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra, (__attribute__((address_space(3))) void*)(&s_a[buf][(32 * w + 4 * i) * kLmRowBytes]),
+          16, voff_a[i], c * kLmRowBytes, 0, 0);
+  };
+
+  // weights: this wave's 4 column tiles
+  const int nt0 = nb * (kLmBN / 16) + w * NTW;
+  const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, NTW * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * p.KC * kSBlockBytes,
+                NTW * p.KC * kSBlockBytes);
+  struct BStage {
+    u32x4 w[NTW];
+    u32x2 s[NTW];
+  };
+  BStage bst[2];
+  auto load_b = [&](BStage& b, int c) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      b.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16,
+                                                      nt * tile_bytes + c * kWBlockBytes,
+                                                      kNonTemporal);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      b.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, col * 8,
+                                                     (nt * p.KC + c) * kSBlockBytes, 0);
+  };
+
+  f32x4 acc[MT][NTW];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  auto compute = [&](int buf, const BStage& b) {
+    const uint8_t* abuf = &s_a[buf][0];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      u32x4 bw[NTW];
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t sw = b.s[nt][g >> 1];
+        const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        bw[nt] = dequant8(b.w[nt][g], sc, -8.0f * sc);
+      }
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = mt * 16 + col;
+        const int slot = (g * 4 + kb) ^ (row & 15);
+        const u32x4 av = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma16(av, bw[nt], acc[mt][nt]);
+      }
+    }
+  };
+
+  // One step: wait for chunk i (its weights were issued before its token
+  // rows, so one count covers both), barrier, refill the buffer freed by
+  // chunk i-1 with chunk i+2, compute chunk i, then reload the weight stage.
+  auto step = [&](int i, BStage& b, bool more) {
+    if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+    __syncthreads();
+    if (more) load_a((i + 2) % 3, c0 + i + 2);
+    compute(i % 3, b);
+    if (more) load_b(b, c0 + i + 2);
+  };
+
+  if (n >= 1) { load_b(bst[0], c0); load_a(0, c0); }
+  if (n >= 2) { load_b(bst[1], c0 + 1); load_a(1, c0 + 1); }
+  int i = 0;
+  for (; i + 3 < n; i += 2) {
+    step(i, bst[0], true);
+    step(i + 1, bst[1], true);
+  }
+  for (; i < n; i += 2) {
+    step(i, bst[0], i + 2 < n);
+    if (i + 1 < n) step(i + 1, bst[1], i + 3 < n);
+  }
+
+  // Output: lane holds tokens 16*mt + 4*kb + r of column col.
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int out = s_out[mt * 16 + kb * 4 + r];
+      if (out < 0) continue;
+      const float t = (p.split == 1 && p.mode == 0 && p.topk_w) ? p.topk_w[out] : 1.0f;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int ncol = (nt0 + nt) * 16 + col;
+        if (p.split > 1)
+          p.ws[((size_t)sp * p.rows_cap + out) * p.N + ncol] = acc[mt][nt][r];
+        else
+          p.c[(size_t)out * p.N + ncol] = (uint16_t)(cvt_pk_bf16(acc[mt][nt][r] * t, 0.f) & 0xFFFFu);
+      }
+    }
+}
+
 template <int TM, int NTW, int WK, int D>
 static int launch_small_m_inst(const GemmParams& gp, unsigned grid, hipStream_t st) {
   hipLaunchKernelGGL((gemm_small_m_kernel<TM, NTW, WK, D>), dim3(grid), dim3(256), 0, st, gp);
@@ -599,6 +820,19 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int64_t grid = tiles_pad * gp.nblocks * gp.split;
   if (grid <= 0) return 0;
   if (grid >= (1ll << 24)) return (int)hipErrorInvalidConfiguration;
+  if (pl.kernel == QMA_KERNEL_LARGE_M) {
+    if (pl.block_m != kLmBM || pl.block_n != kLmBN || L.N % kLmBN != 0)
+      return (int)hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(gemm_large_m_kernel, dim3((unsigned)grid), dim3(256), 0, st, gp);
+    int err = (int)hipGetLastError();
+    if (err == 0 && gp.split > 1) {
+      const int64_t total = (int64_t)gp.num_tiles * gp.BM * (gp.N / 4);
+      const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
+      hipLaunchKernelGGL(splitk_reduce_kernel, dim3(rb), dim3(256), 0, st, gp);
+      err = (int)hipGetLastError();
+    }
+    return err;
+  }
   const int tm = pl.block_m / 16;
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));

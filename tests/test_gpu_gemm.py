@@ -237,8 +237,9 @@ def test_contiguous(gpu, integer):
     a = bf16_small_ints(rng, (m_idx.size, K)) if integer else wl["a"]
     a_poison = a.copy()
     a_poison[m_idx < 0] = 0x7FC0                             # padding rows are never read
-    for override in (None, {"block_m": 16, "block_n": 64, "waves_k": 4},
-                     {"block_m": 32, "block_n": 128, "waves_k": 2}, {"split_k": 2}):
+    for override in (None, {"kernel": 1, "block_m": 16, "block_n": 64, "waves_k": 4},
+                     {"kernel": 1, "block_m": 32, "block_n": 128, "waves_k": 2},
+                     {"split_k": 2}):
         got = contiguous(a_poison, m_idx, w, s, override)
         ref = O.grouped_contiguous(a, m_idx, w, s)
         valid = m_idx >= 0
@@ -273,18 +274,79 @@ def test_masked(gpu, integer):
 
 
 def test_indexed_equals_contiguous_on_same_rows(gpu):
-    E, K, N = 4, 512, 128
+    # The same rows through the indexed and the contiguous routing give the
+    # same bits when the same kernel runs them (the per-element arithmetic
+    # does not depend on where a row sits in its tile).
+    E, K, N = 4, 512, 256
     rng = np.random.default_rng(40)
     counts = [20, 3, 0, 45]
     wl = inputs.make_contiguous("c", 4, E, 0, K, N // 2, counts=counts, weights=False)
     m_idx = wl["m_indices"]
     w, s = weights(rng, E, N, K)
-    got_c = contiguous(wl["a"], m_idx, w, s)
     ids = np.where(m_idx >= 0, m_idx, -1).astype(np.int32)[:, None]
-    got_i, _ = indexed(wl["a"], 1, ids, w, s)
     valid = m_idx >= 0
+    small = {"kernel": 1, "block_m": 16, "block_n": 64, "waves_k": 4, "split_k": 1}
+    got_c = contiguous(wl["a"], m_idx, w, s, small)
+    got_i, _ = indexed(wl["a"], 1, ids, w, s, force_bm=16, override=small)
     assert_per_expert(got_c, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx)
-    np.testing.assert_array_equal(O.bf16_to_f64(got_c[valid]), O.bf16_to_f64(got_i[valid]))
+    assert np.array_equal(got_c[valid], got_i[valid])
+    got_cl = contiguous(wl["a"], m_idx, w, s, {"split_k": 1})          # large-M
+    got_il, pl = indexed(wl["a"], 1, ids, w, s, force_bm=128, override={"split_k": 1})
+    assert pl.kernel == qma.KERNEL_LARGE_M
+    assert_per_expert(got_cl, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx)
+    assert np.array_equal(got_cl[valid], got_il[valid])
+
+
+LARGE_SHAPES = [  # (E, T, topk, K, N): >= 80 rows per expert
+    (3, 300, 1, 512, 512),
+    (2, 200, 2, 1024, 256),
+    (4, 130, 3, 256, 768),
+]
+
+
+@pytest.mark.parametrize("shape", LARGE_SHAPES)
+def test_large_m_integer_exact_bitwise(gpu, shape):
+    E, T, topk, K, N = shape
+    rng = np.random.default_rng(50 + E)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    got, plan = indexed(a, topk, ids, w, s)
+    assert plan.kernel == qma.KERNEL_LARGE_M and plan.block_m == 128
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(got[valid], rne(ref[valid]))
+    assert np.all(got[~valid] == SENT)
+    split, _ = indexed(a, topk, ids, w, s, override={"split_k": 2})
+    assert np.array_equal(split, got)
+
+
+@pytest.mark.parametrize("shape", LARGE_SHAPES)
+def test_large_m_random_within_tolerance(gpu, shape):
+    E, T, topk, K, N = shape
+    rng = np.random.default_rng(60 + E)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    tw = rng.random(T * topk).astype(np.float32)
+    got, plan = indexed(a, topk, ids, w, s, topk_w=tw)
+    assert plan.kernel == qma.KERNEL_LARGE_M
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s, topk_weights=tw)
+    assert_per_expert(got, ref, slot_experts(ids, E), f"large-M {shape}")
+
+
+def test_large_m_nan_poisoned_padding(gpu):
+    E, T, topk, K, N = 4, 300, 1, 512, 256
+    rng = np.random.default_rng(70)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, 3, (T, topk)).astype(np.int32)   # expert 3: no tokens
+    ids[:7] = -1                                             # rows not on this rank
+    s_p = s.copy(); s_p[3] = 0x7FC0
+    a_p = a.copy(); a_p[:7] = 0x7FC0
+    got, plan = indexed(a_p, topk, ids, w, s_p, force_bm=128)
+    assert plan.kernel == qma.KERNEL_LARGE_M
+    assert_per_expert(got, O.moe_gemm_by_slot(a, topk, ids, w, s), slot_experts(ids, E))
 
 
 # ---- the chained layer and graph capture ---------------------------------
