@@ -11,9 +11,9 @@
 // K chunk kc, one 1 KiB block holds the uint4 values in MFMA fragment order:
 // lane l (0..63) owns 16 bytes = 4 words; word j covers row nt*16 + l%16,
 // K range kc*128 + j*32 + (l/16)*8 .. +7. Inside a word the eight values sit
-// in the order (k0, k2, k4, k6, k1, k3, k5, k7) from the low nibble up, so
-// that (w >> 4p) & 0x000F000F isolates the pair (k2p, k2p+1), one per
-// 16-bit half. A second region holds the scales: per (e, nt, kc) 128 bytes
+// in the order (k0, k4, k1, k5, k2, k6, k3, k7) from the low nibble up, so
+// that w & 0x0F0F0F0F holds k0..k3 and (w >> 4) & 0x0F0F0F0F holds k4..k7,
+// one value per byte. A second region holds the scales: per (e, nt, kc) 128 bytes
 // laid out [16 rows][4 groups] bf16.
 namespace qma {
 

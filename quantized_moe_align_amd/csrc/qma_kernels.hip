@@ -158,11 +158,13 @@ int launch_moe_align(const int32_t* ids, int32_t R, int32_t E, int32_t B,
 // packing: [release] grouped techniques). See qma_internal.h for the layout.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t interleave_nibbles(uint32_t w) {
-  // out nibble p <- in nibble {0,2,4,6,1,3,5,7}[p]
+  // out nibble p <- in nibble {0,4,1,5,2,6,3,7}[p]: the even nibbles then
+  // hold k0..k3 and the odd nibbles k4..k7, so one mask (and one shift)
+  // spreads them over bytes in k order.
   uint32_t r = 0;
 #pragma unroll
   for (int p = 0; p < 8; ++p) {
-    const int src = (p < 4) ? 2 * p : 2 * (p - 4) + 1;
+    const int src = (p & 1) ? 4 + (p >> 1) : (p >> 1);
     r |= ((w >> (4 * src)) & 0xFu) << (4 * p);
   }
   return r;
@@ -316,12 +318,17 @@ __device__ __forceinline__ RowInfo row_info(const GemmParams& p, int tile, int e
   return ri;
 }
 
+// One packed word -> the eight exact bf16 values 128 + q, in k order: the
+// bf16 pattern 0x43qq is 128 + q, so each output word is two value bytes
+// interleaved with the constant 0x43 (v_perm_b32 byte selects).
 __device__ __forceinline__ u32x4 unpack_128q(uint32_t w) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes k0 k1 k2 k3
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes k4 k5 k6 k7
   u32x4 r;
-  r.x = (w & 0x000F000Fu) | 0x43004300u;
-  r.y = ((w >> 4) & 0x000F000Fu) | 0x43004300u;
-  r.z = ((w >> 8) & 0x000F000Fu) | 0x43004300u;
-  r.w = ((w >> 12) & 0x000F000Fu) | 0x43004300u;
+  r.x = __builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u);
+  r.y = __builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u);
+  r.z = __builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u);
+  r.w = __builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u);
   return r;
 }
 
@@ -567,19 +574,21 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) 
 //
 // Workgroup: 4 waves over one 128-token tile and 256 weight columns, each
 // wave owning 64 columns (4 tiles of 16) for all 128 tokens (8 tiles of 16).
-// The token tile is staged in LDS in 128-wide K chunks: each wave copies 32
-// rows with 16-byte direct-to-LDS buffer loads (rows the tile does not use
-// get an out-of-range offset and arrive as zeros without being read). Slot j
-// of LDS row r holds the row's 16-byte segment j ^ (r % 16), so the 16 rows
-// an MFMA operand read touches fall in distinct banks. Three LDS buffers
-// give two chunks of prefetch with one barrier per chunk.
+// The token tile passes through LDS in 128-wide K chunks. Each wave fetches
+// 32 rows into registers two chunks ahead (rows the tile does not use get an
+// out-of-range offset and arrive as zeros without being read) and writes
+// them to one of two LDS buffers one chunk ahead, with one barrier per chunk.
+// Slot j of LDS row r holds the row's 16-byte segment j ^ (r % 16), so the
+// 16 rows an MFMA operand read touches fall in distinct banks.
 //
 // Weights never pass through LDS. Each wave loads its packed fragments
-// directly: one 32-bit word per lane per 16x32 MFMA tile. It dequantises
-// them in registers to bf16((q - 8) * scale), using exact fp32 (q * s - 8 s
-// is one rounding of an exact 12-bit product) and one round to bf16. That
-// work is paid once per 128 tokens. This is the MFMA-bound regime, where
-// the small-M kernel's per-output scale fold would cost more VALU than the
+// directly, one 32-bit word per lane per 16x32 MFMA tile, and dequantises
+// them in registers to bf16((q - 8) s). Two nibbles at a time become exact
+// floats: a byte holding q in 0..15, read as an OCP e4m3 code with
+// power-of-two scale 512, is exactly q. Then q s - 8 s is one fp32 FMA (one
+// rounding of an exact 12-bit product), rounded once more to bf16. The cost
+// is paid once per 128 tokens. This is the MFMA-bound regime, where the
+// small-M kernel's per-output scale fold would cost more VALU than the
 // MFMAs themselves.
 // ---------------------------------------------------------------------------
 constexpr int kLmBM = 128;          // tokens per tile
@@ -595,33 +604,28 @@ __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
 }
 
-// Eight uint4 values of one packed word (nibble order k0 k2 k4 k6 k1 k3 k5 k7)
-// -> eight bf16 (q - 8) * s in k order, as an MFMA operand.
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes: k0 k4 k1 k5
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes: k2 k6 k3 k7
-  const float k0 = __builtin_fmaf((float)(lo & 0xFFu), s, neg8s);
-  const float k4 = __builtin_fmaf((float)((lo >> 8) & 0xFFu), s, neg8s);
-  const float k1 = __builtin_fmaf((float)((lo >> 16) & 0xFFu), s, neg8s);
-  const float k5 = __builtin_fmaf((float)(lo >> 24), s, neg8s);
-  const float k2 = __builtin_fmaf((float)(hi & 0xFFu), s, neg8s);
-  const float k6 = __builtin_fmaf((float)((hi >> 8) & 0xFFu), s, neg8s);
-  const float k3 = __builtin_fmaf((float)((hi >> 16) & 0xFFu), s, neg8s);
-  const float k7 = __builtin_fmaf((float)(hi >> 24), s, neg8s);
-  return u32x4{cvt_pk_bf16(k0, k1), cvt_pk_bf16(k2, k3), cvt_pk_bf16(k4, k5),
-               cvt_pk_bf16(k6, k7)};
+// bytes 2H, 2H+1 of v (each 0..15) -> two exact floats
+template <bool H>
+__device__ __forceinline__ f32x2 byte_pair(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.0f, H);
 }
 
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+// One packed word (k0 k4 k1 k5 k2 k6 k3 k7) -> bf16((q - 8) s) for k0..k7
+// in order.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes k0 k1 k2 k3
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes k4 k5 k6 k7
+  const f32x2 q01 = byte_pair<false>(lo), q23 = byte_pair<true>(lo);
+  const f32x2 q45 = byte_pair<false>(hi), q67 = byte_pair<true>(hi);
+  return u32x4{cvt_pk_bf16(__builtin_fmaf(q01.x, s, neg8s), __builtin_fmaf(q01.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q23.x, s, neg8s), __builtin_fmaf(q23.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q45.x, s, neg8s), __builtin_fmaf(q45.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
 }
 
 __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p) {
   constexpr int NTW = 4, MT = 8;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[3][kLmBufBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][kLmBufBytes];
   __shared__ int32_t s_arow[kLmBM];
   __shared__ int32_t s_out[kLmBM];
 
@@ -643,8 +647,11 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   const int c0 = (int)(((int64_t)sp * p.KC) / p.split);
   const int c1 = (int)(((int64_t)(sp + 1) * p.KC) / p.split);
   const int n = c1 - c0;
+  // chunk to fetch for step j; past the end the last chunk is fetched again
+  // so every step issues the same loads and the wait counts stay exact
+  auto chunk = [&](int j) { return c0 + min(j, n - 1); };
 
-  // token rows: wave w copies rows 32w .. 32w+31, four per instruction
+  // token rows: wave w handles rows 32w .. 32w+31, four per 16-lane group
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
   uint32_t voff_a[8];
 #pragma unroll
@@ -654,12 +661,16 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
     const uint32_t seg = (uint32_t)(col ^ (row & 15));
     voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
-  auto load_a = [&](int buf, int c) {
+  typedef u32x4 AStage[8];
+  auto load_a = [&](AStage& r, int c) {
 #pragma unroll
     for (int i = 0; i < 8; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          ra, (__attribute__((address_space(3))) void*)(&s_a[buf][(32 * w + 4 * i) * kLmRowBytes]),
-          16, voff_a[i], c * kLmRowBytes, 0, 0);
+      r[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[i], c * kLmRowBytes, 0);
+  };
+  auto store_a = [&](const AStage& r, int buf) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *(u32x4*)(&s_a[buf][(32 * w + 4 * i + kb) * kLmRowBytes + col * 16]) = r[i];
   };
 
   // weights: this wave's 4 column tiles
@@ -674,7 +685,6 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
     u32x4 w[NTW];
     u32x2 s[NTW];
   };
-  BStage bst[2];
   auto load_b = [&](BStage& b, int c) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
@@ -707,7 +717,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = mt * 16 + col;
-        const int slot = (g * 4 + kb) ^ (row & 15);
+        const int slot = (g * 4 + kb) ^ col;
         const u32x4 av = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma16(av, bw[nt], acc[mt][nt]);
@@ -715,28 +725,30 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
     }
   };
 
-  // One step: wait for chunk i (its weights were issued before its token
-  // rows, so one count covers both), barrier, refill the buffer freed by
-  // chunk i-1 with chunk i+2, compute chunk i, then reload the weight stage.
-  auto step = [&](int i, BStage& b, bool more) {
-    if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+  // Step j computes chunk j from LDS buffer j % 2 with weight stage b;
+  // token rows for chunk j+1 (fetched one step earlier into a_next) go to
+  // the other buffer, and chunk j+2's rows and weights are fetched.
+  AStage ar0, ar1;
+  BStage bs0, bs1;
+  load_a(ar0, chunk(0));
+  load_b(bs0, chunk(0));
+  load_a(ar1, chunk(1));
+  load_b(bs1, chunk(1));
+  store_a(ar0, 0);
+  __syncthreads();
+  auto step = [&](int j, AStage& a_next, AStage& a_fetch, BStage& b) {
+    load_a(a_fetch, chunk(j + 2));
+    compute(j & 1, b);
+    load_b(b, chunk(j + 2));
+    store_a(a_next, (j + 1) & 1);
     __syncthreads();
-    if (more) load_a((i + 2) % 3, c0 + i + 2);
-    compute(i % 3, b);
-    if (more) load_b(b, c0 + i + 2);
   };
-
-  if (n >= 1) { load_b(bst[0], c0); load_a(0, c0); }
-  if (n >= 2) { load_b(bst[1], c0 + 1); load_a(1, c0 + 1); }
-  int i = 0;
-  for (; i + 3 < n; i += 2) {
-    step(i, bst[0], true);
-    step(i + 1, bst[1], true);
+  int j = 0;
+  for (; j + 1 < n; j += 2) {
+    step(j, ar1, ar0, bs0);
+    step(j + 1, ar0, ar1, bs1);
   }
-  for (; i < n; i += 2) {
-    step(i, bst[0], i + 2 < n);
-    if (i + 1 < n) step(i + 1, bst[1], i + 3 < n);
-  }
+  if (j < n) step(j, ar1, ar0, bs0);
 
   // Output: lane holds tokens 16*mt + 4*kb + r of column col.
 #pragma unroll
