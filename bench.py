@@ -160,6 +160,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="after the run, copy a buffer of this many bytes 3 times (a "
+                         "plain copy kernel of known size, to calibrate rocprofv3 "
+                         "FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the expert GEMM "
@@ -278,6 +282,14 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.copy_bytes > 0:
+        src = torch.empty(args.copy_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        out["copy_calibration_bytes"] = args.copy_bytes
     print(json.dumps(out), flush=True)
 
 

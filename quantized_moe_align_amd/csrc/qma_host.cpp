@@ -77,9 +77,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->kernel = QMA_KERNEL_SMALL_M;
   p->block_m = bm;
   const int tm = bm / 16;
-  // The four waves of a workgroup split K when K is long (each wave still
-  // streams >= 8 chunks of 128) and split the columns otherwise.
-  int wk = L.k_chunks >= 32 ? 4 : (L.k_chunks >= 16 ? 2 : 1);
+  // The four waves of a workgroup split K in two when K is long (each wave
+  // still streams >= 12 chunks of 128) and split the columns otherwise.
+  int wk = L.k_chunks >= 24 ? 2 : 1;
   if (L.N % (16 * (4 / wk)) != 0) wk = 4;
   const int wn = 4 / wk;
   int ntw = 0;

@@ -90,7 +90,7 @@ namespace qma {
 // waves_k of them split K and 4 / waves_k split the columns, so
 // block_n = 16 * NTW * (4 / waves_k). The cross-wave reduction holds up to
 // 4 x NTW x TM KiB of LDS, so TM * NTW <= 8. The prefetch depth (128-wide K
-// chunks in flight per wave) is sized to a ~200 VGPR budget.
+// chunks in flight per wave) is sized to a ~160 VGPR budget.
 constexpr bool small_m_supported(int tm, int ntw) {
   return (tm == 1 || tm == 2 || tm == 4) && (ntw == 1 || ntw == 2 || ntw == 4) &&
          tm * ntw <= 8;
@@ -98,7 +98,7 @@ constexpr bool small_m_supported(int tm, int ntw) {
 constexpr int small_m_depth(int tm, int ntw) {
   const int per = ntw * 6 + tm * 16;
   const int fixed = ntw * tm * 4 + tm * 4 + 30;
-  const int d = (200 - fixed) / per;
+  const int d = (160 - fixed) / per;
   return d < 2 ? 2 : (d > 4 ? 4 : d);
 }
 }  // namespace qma

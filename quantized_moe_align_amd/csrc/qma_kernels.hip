@@ -280,8 +280,10 @@ __device__ __forceinline__ int tile_expert(const GemmParams& p, int tile) {
     const int e = p.m_indices[tile * p.BM];
     return (e >= 0 && e < p.E) ? e : -1;
   }
-  const int e = tile / p.tiles_per_expert;
-  const int jt = tile - e * p.tiles_per_expert;
+  // masked: tiles are numbered row-block-major (tile = jt * E + e), so the
+  // tiles that hold rows come first and spread evenly over the XCDs
+  const int e = tile % p.E;
+  const int jt = tile / p.E;
   const int mm = min(max(p.masked_m[e], 0), p.Mb);
   return (jt * p.BM < mm) ? e : -1;
 }
@@ -306,7 +308,7 @@ __device__ __forceinline__ RowInfo row_info(const GemmParams& p, int tile, int e
       ri.out_row = row;
     }
   } else {
-    const int jt = tile - e * p.tiles_per_expert;
+    const int jt = tile / p.E;
     const int mm = min(max(p.masked_m[e], 0), p.Mb);
     const int rr = jt * p.BM + r;
     if (rr < mm) {

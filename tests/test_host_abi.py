@@ -88,7 +88,7 @@ def _plan(E, N, K, T, topk, force=0):
 def test_plan_decode_ep8():
     p = _plan(48, 4096, 7168, 576, 1)
     assert p.kernel == qma.KERNEL_SMALL_M and p.block_m == 16
-    assert p.block_n == 64 and p.waves_k == 4 and p.split_k == 1  # 48 x 64 tiles
+    assert p.block_n == 128 and p.waves_k == 2 and p.split_k == 1  # 48 x 32 tiles
     assert p.tok_e_x100 == 1200 and p.rows == 576
     assert qma.qma_workspace_bytes(p) == 0
 
@@ -101,7 +101,7 @@ def test_plan_tp8_and_tiny():
     assert t.block_n == 128                            # 16 tiles: the narrower width
     assert t.split_k == 1                              # K = 256: no room to split
     d = _plan(48, 7168, 2048, 576, 1)                  # EP8 down: K = 2048
-    assert d.waves_k == 2 and d.block_n == 128 and d.split_k == 1
+    assert d.waves_k == 1 and d.block_n == 256 and d.split_k == 1
 
 
 def test_block_m_follows_tok_e():
@@ -110,15 +110,15 @@ def test_block_m_follows_tok_e():
 
 
 def test_split_k_gate_turns_on_only_when_underfilled():
-    # 1 expert: 64 tiles at 64 columns, 128 at 32 < 256 CUs -> split
+    # 1 expert: 32 tiles at 128 columns, 64 at 64 < 256 CUs -> split
     p = _plan(1, 4096, 7168, 12, 1)
-    assert p.block_n == 32 and p.est_tiles == 128 and p.split_k == 2
+    assert p.block_n == 64 and p.est_tiles == 64 and p.split_k == 4
     assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
-    # 2 experts: the 32-column width gives exactly 256 tiles -> no split
-    assert _plan(2, 4096, 7168, 24, 1).split_k == 1
-    # EP32 share: 12 experts x 64 tiles = 768 >= 256 -> full width, no split
+    # 4 experts: the 64-column width gives exactly 256 tiles -> no split
+    assert _plan(4, 4096, 7168, 48, 1).split_k == 1
+    # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> full width, no split
     q = _plan(12, 4096, 7168, 144, 1)
-    assert q.split_k == 1 and q.block_n == 64
+    assert q.split_k == 1 and q.block_n == 128
 
 
 def test_plan_rejects_bad_force_and_wrong_path():
