@@ -161,11 +161,11 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * wider tile only when enough N tiles exist), and split-K turns on only
  * when the grid would underfill the compute units ([release] indexed
  * techniques: the stream-K gate). force_block_m = 0 lets the planner choose;
- * otherwise it must be 16, 32, 48 or 64 (small-M) or 64, 128 or 256
- * (large-M, when the planner picks large-M). The down projection passes
- * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,
- * a bad force_block_m, or a layer whose path is not INDEXED ->
- * QMA_ERR_INVALID_ARG. */
+ * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128
+ * or 256 the large-M kernel (which needs N % 256 == 0). The down projection
+ * passes gate_up's block_m so one moe_align serves both. Errors: T < 0,
+ * topk < 1, a force_block_m outside {0,16,32,64,128,256}, 128/256 with
+ * N % 256 != 0, or a layer whose path is not INDEXED -> QMA_ERR_INVALID_ARG. */
 qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
                             int32_t force_block_m, qma_plan_t* out);
 

@@ -17,8 +17,12 @@ SOURCES = [os.path.join(HERE, "csrc", "qma_host.cpp"),
            os.path.join(HERE, "csrc", "qma_kernels.hip")]
 ARCH = "gfx950"
 
-# Packed-FP32 VALU forms are disabled for all device code.
-DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Packed-FP32 VALU forms are disabled for all device code. MFMA accumulators
+# are kept in architectural VGPRs: the 128-token GEMM tile fits there, and
+# the AGPR form made the register allocator shuffle accumulators every
+# iteration.
+DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                "-mllvm", "-amdgpu-mfma-vgpr-form"]
 
 
 def hipcc() -> str:

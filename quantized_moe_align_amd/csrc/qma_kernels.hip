@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <type_traits>
 
 #include "qma_internal.h"
 
@@ -625,11 +626,37 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
                cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
 }
 
+// Bare workgroup barrier. __syncthreads() also fences memory, and that
+// fence waits for every outstanding direct-to-LDS load, including prefetches
+// of later chunks. The waits this kernel needs are explicit vmcnt counts,
+// and the asm clobbers keep the compiler from moving memory operations
+// across the barrier.
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// MT = 16-token tiles per workgroup (8 or 16: 128- or 256-token tiles).
+template <int MT>
 __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p) {
-  constexpr int NTW = 4, MT = 8;
-  __shared__ __attribute__((aligned(1024))) uint8_t s_a[2][kLmBufBytes];
-  __shared__ int32_t s_arow[kLmBM];
-  __shared__ int32_t s_out[kLmBM];
+  constexpr int NTW = 4;
+  constexpr int BM = MT * 16;
+  constexpr int ROWS_W = BM / 4;           // rows each wave copies per chunk
+  constexpr int NA = ROWS_W / 4;           // 16-byte copies per lane per chunk
+  // Token-tile LDS buffers: two separate objects, so the compiler's wait
+  // counts can tell a load into one buffer from a read of the other.
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a0[BM * kLmRowBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a1[BM * kLmRowBytes];
+  __shared__ int32_t s_arow[BM];
+  __shared__ int32_t s_out[BM];
 
   int tile, nb, sp;
   if (!decode_bid(p, tile, nb, sp)) return;
@@ -639,10 +666,10 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int col = lane & 15, kb = lane >> 4;
 
-  if (threadIdx.x < kLmBM) {
-    const RowInfo ri = row_info(p, tile, e, threadIdx.x);
-    s_arow[threadIdx.x] = ri.valid ? ri.a_row : -1;
-    s_out[threadIdx.x] = ri.valid ? ri.out_row : -1;
+  for (int r = threadIdx.x; r < BM; r += 256) {
+    const RowInfo ri = row_info(p, tile, e, r);
+    s_arow[r] = ri.valid ? ri.a_row : -1;
+    s_out[r] = ri.valid ? ri.out_row : -1;
   }
   __syncthreads();
 
@@ -653,27 +680,37 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   // so every step issues the same loads and the wait counts stay exact
   auto chunk = [&](int j) { return c0 + min(j, n - 1); };
 
-  // token rows: wave w handles rows 32w .. 32w+31, four per 16-lane group
+  // Token rows: wave w copies rows w*ROWS_W .. +ROWS_W-1, four rows (one
+  // per 16-lane group) per direct-to-LDS instruction; lane l lands in slot
+  // l % 16 of its row, which holds the row's segment (l % 16) ^ (row % 16).
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-  uint32_t voff_a[8];
+  uint32_t voff_a[NA];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int row = 32 * w + 4 * i + kb;
+  for (int i = 0; i < NA; ++i) {
+    const int row = w * ROWS_W + 4 * i + kb;
     const int ar = s_arow[row];
     const uint32_t seg = (uint32_t)(col ^ (row & 15));
     voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
-  typedef u32x4 AStage[8];
-  auto load_a = [&](AStage& r, int c) {
+  // (the LDS address is formed from the __shared__ array itself, which the
+  // host compilation pass can type-check)
+  auto load_a = [&](auto buf_id, int c) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      r[i] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_a[i], c * kLmRowBytes, 0);
+    for (int i = 0; i < NA; ++i) {
+      const int off = (w * ROWS_W + 4 * i) * kLmRowBytes;
+      const int vo = (int)voff_a[i];
+      if constexpr (decltype(buf_id)::value == 0)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(s_a0 + off), 16, vo,
+            c * kLmRowBytes, 0, 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(s_a1 + off), 16, vo,
+            c * kLmRowBytes, 0, 0);
+    }
   };
-  auto store_a = [&](const AStage& r, int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *(u32x4*)(&s_a[buf][(32 * w + 4 * i + kb) * kLmRowBytes + col * 16]) = r[i];
-  };
+  using B0 = std::integral_constant<int, 0>;
+  using B1 = std::integral_constant<int, 1>;
 
   // weights: this wave's 4 column tiles
   const int nt0 = nb * (kLmBN / 16) + w * NTW;
@@ -705,8 +742,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf, const BStage& b) {
-    const uint8_t* abuf = &s_a[buf][0];
+  auto compute = [&](const uint8_t* abuf, const BStage& b) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       u32x4 bw[NTW];
@@ -727,30 +763,43 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
     }
   };
 
-  // Step j computes chunk j from LDS buffer j % 2 with weight stage b;
-  // token rows for chunk j+1 (fetched one step earlier into a_next) go to
-  // the other buffer, and chunk j+2's rows and weights are fetched.
-  AStage ar0, ar1;
+  // Issue order per step j: [wait, barrier] token rows of chunk j+1 (into
+  // the buffer chunk j-1 used), compute chunk j, weights of chunk j+2.
+  // Chunk j's token rows are therefore followed by exactly chunk j+1's
+  // weights (8 loads) when step j waits for them.
   BStage bs0, bs1;
-  load_a(ar0, chunk(0));
   load_b(bs0, chunk(0));
-  load_a(ar1, chunk(1));
+  load_a(B0{}, chunk(0));
+  __builtin_amdgcn_sched_barrier(0);
   load_b(bs1, chunk(1));
-  store_a(ar0, 0);
-  __syncthreads();
-  auto step = [&](int j, AStage& a_next, AStage& a_fetch, BStage& b) {
-    load_a(a_fetch, chunk(j + 2));
-    compute(j & 1, b);
+  // step on chunk j: `cur` is j's buffer (0 or 1), the other gets chunk j+1.
+  // The last step waits for everything, since the count of loads issued
+  // after its token rows is not fixed there.
+  auto step = [&](int j, auto cur, BStage& b) {
+    if (j + 1 < n)
+      wait_vmcnt<8>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    // (sched barriers keep the weight prefetch behind the token-row loads)
+    if constexpr (decltype(cur)::value == 0) {
+      load_a(B1{}, chunk(j + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(&s_a0[0], b);
+    } else {
+      load_a(B0{}, chunk(j + 1));
+      __builtin_amdgcn_sched_barrier(0);
+      compute(&s_a1[0], b);
+    }
     load_b(b, chunk(j + 2));
-    store_a(a_next, (j + 1) & 1);
-    __syncthreads();
   };
-  int j = 0;
-  for (; j + 1 < n; j += 2) {
-    step(j, ar1, ar0, bs0);
-    step(j + 1, ar0, ar1, bs1);
+  for (int j = 0;; j += 2) {
+    step(j, B0{}, bs0);
+    if (j + 1 >= n) break;
+    step(j + 1, B1{}, bs1);
+    if (j + 2 >= n) break;
   }
-  if (j < n) step(j, ar1, ar0, bs0);
+  wait_vmcnt<0>();
 
   // Output: lane holds tokens 16*mt + 4*kb + r of column col.
 #pragma unroll
@@ -769,6 +818,12 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
           p.c[(size_t)out * p.N + ncol] = (uint16_t)(cvt_pk_bf16(acc[mt][nt][r] * t, 0.f) & 0xFFFFu);
       }
     }
+}
+
+template <int MT>
+static int launch_large_m_inst(const GemmParams& gp, unsigned grid, hipStream_t st) {
+  hipLaunchKernelGGL((gemm_large_m_kernel<MT>), dim3(grid), dim3(256), 0, st, gp);
+  return (int)hipGetLastError();
 }
 
 template <int TM, int NTW, int WK, int D>
@@ -835,10 +890,10 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   if (grid <= 0) return 0;
   if (grid >= (1ll << 24)) return (int)hipErrorInvalidConfiguration;
   if (pl.kernel == QMA_KERNEL_LARGE_M) {
-    if (pl.block_m != kLmBM || pl.block_n != kLmBN || L.N % kLmBN != 0)
+    if ((pl.block_m != 128 && pl.block_m != 256) || pl.block_n != kLmBN || L.N % kLmBN != 0)
       return (int)hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(gemm_large_m_kernel, dim3((unsigned)grid), dim3(256), 0, st, gp);
-    int err = (int)hipGetLastError();
+    int err = pl.block_m == 256 ? launch_large_m_inst<16>(gp, (unsigned)grid, st)
+                                : launch_large_m_inst<8>(gp, (unsigned)grid, st);
     if (err == 0 && gp.split > 1) {
       const int64_t total = (int64_t)gp.num_tiles * gp.BM * (gp.N / 4);
       const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);
