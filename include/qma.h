@@ -162,15 +162,19 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * when the grid would underfill the compute units ([release] indexed
  * techniques: the stream-K gate). force_block_m = 0 lets the planner choose;
  * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128
- * or 256 the large-M kernel (which needs N % 256 == 0). The down projection
- * passes gate_up's block_m so one moe_align serves both. Errors: T < 0,
- * topk < 1, a force_block_m outside {0,16,32,64,128,256}, 128/256 with
- * N % 256 != 0, or a layer whose path is not INDEXED -> QMA_ERR_INVALID_ARG. */
+ * the large-M kernel (which needs N % 256 == 0). The down projection passes
+ * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,
+ * a force_block_m outside {0,16,32,64,128}, 128 with N % 256 != 0, or a
+ * layer whose path is not INDEXED -> QMA_ERR_INVALID_ARG. */
 qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
                             int32_t force_block_m, qma_plan_t* out);
 
 /* Plan a grouped GEMM. Contiguous layers: m_rows_or_budget = M, the padded
- * row count (a multiple of 128), and expected_m is ignored. Masked layers:
+ * row count (a multiple of 128), and expected_m is ignored; the large-M
+ * kernel is used whenever N % 256 == 0, since each 128-row tile belongs to
+ * one expert ([release] grouped techniques: contiguous prefill pads each
+ * expert to a 128-row boundary).
+ * Masked layers:
  * m_rows_or_budget = the per-expert row budget, and expected_m = the
  * host-side estimate of valid rows that picks block_m ([release] grouped
  * techniques: BLOCK_M from the expected token count). */

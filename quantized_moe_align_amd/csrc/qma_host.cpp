@@ -159,9 +159,8 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
   if (plan->kernel != QMA_KERNEL_SMALL_M && plan->kernel != QMA_KERNEL_LARGE_M)
     return fail(QMA_ERR_INVALID_ARG, "plan has unknown kernel %d", plan->kernel);
   if (plan->kernel == QMA_KERNEL_LARGE_M &&
-      ((plan->block_m != 128 && plan->block_m != 256) || plan->block_n != 256 ||
-       L.N % 256 != 0))
-    return fail(QMA_ERR_INVALID_ARG, "large-M plan needs block 128 or 256 x 256 and N %% 256 == 0");
+      (plan->block_m != 128 || plan->block_n != 256 || L.N % 256 != 0))
+    return fail(QMA_ERR_INVALID_ARG, "large-M plan needs block 128 x 256 and N %% 256 == 0");
   if (plan->block_m < 16 || plan->block_m % 16 != 0 ||
       (plan->kernel == QMA_KERNEL_SMALL_M && plan->block_m > 64))
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
@@ -294,19 +293,18 @@ qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
   out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
   const int64_t e_active = std::min<int64_t>(L.E, std::max<int64_t>(R, 1));
   if (force_block_m != 0 && force_block_m != 16 && force_block_m != 32 &&
-      force_block_m != 64 && force_block_m != 128 && force_block_m != 256)
-    return fail(QMA_ERR_INVALID_ARG, "force_block_m %d not in {16,32,64,128,256}", force_block_m);
-  if (force_block_m >= 128 && !large_m_fits(L))
+      force_block_m != 64 && force_block_m != 128)
+    return fail(QMA_ERR_INVALID_ARG, "force_block_m %d not in {16,32,64,128}", force_block_m);
+  if (force_block_m == 128 && !large_m_fits(L))
     return fail(QMA_ERR_INVALID_ARG, "block_m %d needs N %% 256 == 0 (N=%d)", force_block_m, L.N);
   // At or above 80 routed rows per expert the large-M kernel amortises the
   // dequantisation over 128 tokens; below, the small-M kernel takes the
   // smallest of 16, 32, 64 rows that covers tok_e.
-  const bool large = force_block_m >= 128 ||
+  const bool large = force_block_m == 128 ||
                      (force_block_m == 0 && tok_e >= 80.0 && large_m_fits(L));
   if (large) {
-    const int32_t lbm = force_block_m >= 128 ? force_block_m : 128;
-    const int64_t per_e = std::max<int64_t>(1, ceil_div((int64_t)std::ceil(tok_e), lbm));
-    plan_large_m(L, lbm, (int32_t)std::min<int64_t>(e_active * per_e, 1 << 30), out);
+    const int64_t per_e = std::max<int64_t>(1, ceil_div((int64_t)std::ceil(tok_e), 128));
+    plan_large_m(L, 128, (int32_t)std::min<int64_t>(e_active * per_e, 1 << 30), out);
     return ok();
   }
   const int32_t bm = force_block_m != 0 ? force_block_m
@@ -328,7 +326,10 @@ qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
     out->rows = M;
     const double tok_e = (double)M / L.E;
     out->tok_e_x100 = (int32_t)std::lround(tok_e * 100.0);
-    if (tok_e >= 80.0 && large_m_fits(L))
+    // Every expert's rows come padded to a multiple of 128, so each 128-row
+    // tile holds one expert and the large-M kernel applies whenever N allows,
+    // however many experts are empty (M/E says nothing about that).
+    if (large_m_fits(L))
       plan_large_m(L, 128, std::max(1, M / 128), out);
     else
       plan_small_m(L, 64, std::max(1, M / 64), out);

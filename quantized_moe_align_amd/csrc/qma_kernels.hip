@@ -576,31 +576,45 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) 
 // Large-M expert GEMM (prefill shapes: 128-token tiles).
 //
 // Workgroup: 4 waves over one 128-token tile and 256 weight columns, each
-// wave owning 64 columns (4 tiles of 16) for all 128 tokens (8 tiles of 16).
-// The token tile passes through LDS in 128-wide K chunks. Each wave fetches
-// 32 rows into registers two chunks ahead (rows the tile does not use get an
-// out-of-range offset and arrive as zeros without being read) and writes
-// them to one of two LDS buffers one chunk ahead, with one barrier per chunk.
-// Slot j of LDS row r holds the row's 16-byte segment j ^ (r % 16), so the
-// 16 rows an MFMA operand read touches fall in distinct banks.
+// wave owning 64 columns for all 128 tokens as 4 x 2 tiles of 32 x 32
+// (v_mfma_f32_32x32x16_bf16). The 32 x 32 form is chosen over 16 x 16 x 32
+// because it leaves more issue slots per flop for the dequantisation VALU
+// work and halves the token-fragment reads per weight column pair; this
+// kernel is issue-bound on those, not on the matrix core.
 //
-// Weights never pass through LDS. Each wave loads its packed fragments
-// directly, one 32-bit word per lane per 16x32 MFMA tile, and dequantises
-// them in registers to bf16((q - 8) s). Two nibbles at a time become exact
-// floats: a byte holding q in 0..15, read as an OCP e4m3 code with
-// power-of-two scale 512, is exactly q. Then q s - 8 s is one fp32 FMA (one
-// rounding of an exact 12-bit product), rounded once more to bf16. The cost
-// is paid once per 128 tokens. This is the MFMA-bound regime, where the
-// small-M kernel's per-output scale fold would cost more VALU than the
-// MFMAs themselves.
+// Token tile: passes through LDS in 128-wide K chunks, fetched by
+// direct-to-LDS buffer loads (16 bytes per lane, four rows per instruction)
+// into one of two buffers one chunk ahead, with one barrier per chunk. Slot
+// j of LDS row r holds the row's 16-byte segment j ^ (r % 16), so the rows an
+// operand read touches fall in distinct banks. Rows the tile does not use get
+// an out-of-range offset and arrive as zeros without being read.
+//
+// Weights never pass through LDS. The packed layout is the 16-column one the
+// small-M kernel reads (lane l of a 16x128 tile holds column l % 16, K rows
+// 8(l/16)..+7 of each 32-row group); a 32 x 32 x 16 operand needs column
+// l % 32, K rows 8(l/32)..+7 of a 16-row half, which is lane
+// (l % 16) + 16 (2h + l/32) of 16-column tile (l % 32)/16, so each lane
+// loads that lane's 16 bytes (one word per group) for h = 0 and 1. Words are
+// dequantised in registers to bf16((q - 8) s): two nibbles at a time become
+// exact floats (a byte holding q in 0..15, read as an OCP e4m3 code with
+// power-of-two scale 512, is exactly q), then q s - 8 s is one fp32 FMA
+// rounded once more to bf16. The cost is paid once per 128 tokens.
 // ---------------------------------------------------------------------------
 constexpr int kLmBM = 128;          // tokens per tile
 constexpr int kLmBN = 256;          // columns per workgroup
 constexpr int kLmRowBytes = 256;    // one 128-wide K chunk of a bf16 row
-constexpr int kLmBufBytes = kLmBM * kLmRowBytes;
+constexpr int kLmMT = kLmBM / 32;   // 32-row tiles per wave
+constexpr int kLmNT = 2;            // 32-column tiles per wave
+constexpr int kLmBLoads = 3 * kLmNT;  // weight + scale loads per chunk and wave
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
 
 __device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
   const f32x2 v = {lo, hi};
@@ -626,11 +640,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
                cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
 }
 
-// Bare workgroup barrier. __syncthreads() also fences memory, and that
-// fence waits for every outstanding direct-to-LDS load, including prefetches
-// of later chunks. The waits this kernel needs are explicit vmcnt counts,
-// and the asm clobbers keep the compiler from moving memory operations
-// across the barrier.
 // s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -638,19 +647,21 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// Bare workgroup barrier. __syncthreads() also fences memory, and that
+// fence waits for every outstanding direct-to-LDS load, including prefetches
+// of later chunks. The waits this kernel needs are explicit vmcnt counts,
+// and the asm clobbers keep the compiler from moving memory operations
+// across the barrier.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
-// MT = 16-token tiles per workgroup (8 or 16: 128- or 256-token tiles).
-template <int MT>
-__global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p) {
-  constexpr int NTW = 4;
-  constexpr int BM = MT * 16;
-  constexpr int ROWS_W = BM / 4;           // rows each wave copies per chunk
-  constexpr int NA = ROWS_W / 4;           // 16-byte copies per lane per chunk
+__global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p) {
+  constexpr int BM = kLmBM;
+  constexpr int ROWS_W = BM / 4;           // token rows each wave copies per chunk
+  constexpr int NA = ROWS_W / 4;           // direct-to-LDS loads per lane per chunk
   // Token-tile LDS buffers: two separate objects, so the compiler's wait
   // counts can tell a load into one buffer from a read of the other.
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[BM * kLmRowBytes];
@@ -664,7 +675,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   if (e < 0) return;
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int col = lane & 15, kb = lane >> 4;
+  const int c16 = lane & 15, kq = lane >> 5, l32 = lane & 31;
 
   for (int r = threadIdx.x; r < BM; r += 256) {
     const RowInfo ri = row_info(p, tile, e, r);
@@ -681,15 +692,15 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   auto chunk = [&](int j) { return c0 + min(j, n - 1); };
 
   // Token rows: wave w copies rows w*ROWS_W .. +ROWS_W-1, four rows (one
-  // per 16-lane group) per direct-to-LDS instruction; lane l lands in slot
-  // l % 16 of its row, which holds the row's segment (l % 16) ^ (row % 16).
+  // per 16-lane group) per instruction; lane l lands in slot l % 16 of its
+  // row, which holds the row's segment (l % 16) ^ (row % 16).
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
   uint32_t voff_a[NA];
 #pragma unroll
   for (int i = 0; i < NA; ++i) {
-    const int row = w * ROWS_W + 4 * i + kb;
+    const int row = w * ROWS_W + 4 * i + (lane >> 4);
     const int ar = s_arow[row];
-    const uint32_t seg = (uint32_t)(col ^ (row & 15));
+    const uint32_t seg = (uint32_t)(c16 ^ (row & 15));
     voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
   // (the LDS address is formed from the __shared__ array itself, which the
@@ -712,53 +723,86 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   using B0 = std::integral_constant<int, 0>;
   using B1 = std::integral_constant<int, 1>;
 
-  // weights: this wave's 4 column tiles
-  const int nt0 = nb * (kLmBN / 16) + w * NTW;
+  // Weights: this wave's 64 columns are 16-column packed tiles nt16..+3;
+  // 32-column tile t uses packed tiles 2t and 2t+1.
+  const int nt16 = nb * (kLmBN / 16) + w * 4;
   const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
   const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, NTW * tile_bytes);
+      make_rsrc(p.wpk + ((size_t)e * p.NT + nt16) * tile_bytes, 4 * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * p.KC * kSBlockBytes,
-                NTW * p.KC * kSBlockBytes);
+      make_rsrc(p.spk + ((size_t)e * p.NT + nt16) * p.KC * kSBlockBytes,
+                4 * p.KC * kSBlockBytes);
+  const int half16 = (lane >> 4) & 1;  // which 16-column tile of the 32
+  const uint32_t voff_w = half16 * tile_bytes + (uint32_t)(c16 + 16 * kq) * 16u;
+  const uint32_t voff_s = half16 * p.KC * kSBlockBytes + c16 * 8;
   struct BStage {
-    u32x4 w[NTW];
-    u32x2 s[NTW];
+    u32x4 w[kLmNT][2];  // [32-column tile][K half]: one word per 32-row group
+    u32x2 s[kLmNT];     // four group scales of the lane's column
   };
   auto load_b = [&](BStage& b, int c) {
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-      b.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16,
-                                                      nt * tile_bytes + c * kWBlockBytes,
-                                                      kNonTemporal);
+    for (int t = 0; t < kLmNT; ++t)
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt)
-      b.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, col * 8,
-                                                     (nt * p.KC + c) * kSBlockBytes, 0);
+      for (int h = 0; h < 2; ++h)
+        b.w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(
+            rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, kNonTemporal);
+#pragma unroll
+    for (int t = 0; t < kLmNT; ++t)
+      b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
+                                                    (2 * t * p.KC + c) * kSBlockBytes, 0);
   };
 
-  f32x4 acc[MT][NTW];
+  f32x16 acc[kLmMT][kLmNT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+  for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int t = 0; t < kLmNT; ++t) acc[mt][t] = f32x16{};
 
+  // One chunk: 8 K steps of 16; step ks uses group g = ks / 2, half ks % 2.
+  // Software-pipelined one step deep: the token fragments and dequantised
+  // weights of step ks+1 are fetched and computed while step ks's MFMAs run,
+  // so a wave alone on its SIMD does not wait out LDS latency.
   auto compute = [&](const uint8_t* abuf, const BStage& b) {
+    auto frags = [&](u32x4 (&av)[kLmMT], int ks) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      u32x4 bw[NTW];
+      for (int mt = 0; mt < kLmMT; ++mt) {
+        const int row = mt * 32 + l32;
+        const int slot = (2 * ks + kq) ^ (row & 15);
+        av[mt] = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
+      }
+    };
+    auto deq = [&](u32x4 (&bw)[kLmNT], int ks) {
+      const int g = ks >> 1, h = ks & 1;
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const uint32_t sw = b.s[nt][g >> 1];
+      for (int t = 0; t < kLmNT; ++t) {
+        const uint32_t sw = b.s[t][g >> 1];
         const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        bw[nt] = dequant8(b.w[nt][g], sc, -8.0f * sc);
+        bw[t] = dequant8(b.w[t][h][g], sc, -8.0f * sc);
+      }
+    };
+    u32x4 av[2][kLmMT], bw[2][kLmNT];
+    frags(av[0], 0);
+    deq(bw[0], 0);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const int cur = ks & 1;
+      if (ks < 7) {
+        frags(av[cur ^ 1], ks + 1);
+        deq(bw[cur ^ 1], ks + 1);
       }
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int row = mt * 16 + col;
-        const int slot = (g * 4 + kb) ^ col;
-        const u32x4 av = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
+      for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) acc[mt][nt] = mfma16(av, bw[nt], acc[mt][nt]);
+        for (int t = 0; t < kLmNT; ++t) acc[mt][t] = mfma32(av[cur][mt], bw[cur][t], acc[mt][t]);
+      if (ks < 7) {
+        // next step's fragment reads first, then each MFMA followed by a
+        // share of the next step's dequantisation
+        __builtin_amdgcn_sched_group_barrier(0x100, kLmMT, 0);
+#pragma unroll
+        for (int i = 0; i < kLmMT * kLmNT; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
       }
     }
   };
@@ -766,7 +810,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   // Issue order per step j: [wait, barrier] token rows of chunk j+1 (into
   // the buffer chunk j-1 used), compute chunk j, weights of chunk j+2.
   // Chunk j's token rows are therefore followed by exactly chunk j+1's
-  // weights (8 loads) when step j waits for them.
+  // weights (kLmBLoads loads) when step j waits for them.
   BStage bs0, bs1;
   load_b(bs0, chunk(0));
   load_a(B0{}, chunk(0));
@@ -777,7 +821,7 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   // after its token rows is not fixed there.
   auto step = [&](int j, auto cur, BStage& b) {
     if (j + 1 < n)
-      wait_vmcnt<8>();
+      wait_vmcnt<kLmBLoads>();
     else
       wait_vmcnt<0>();
     lds_barrier();
@@ -801,29 +845,75 @@ __global__ __launch_bounds__(256, 1) void gemm_large_m_kernel(const GemmParams p
   }
   wait_vmcnt<0>();
 
-  // Output: lane holds tokens 16*mt + 4*kb + r of column col.
+  // Output. Accumulator element 4i + r of tile (mt, t) is token
+  // 32 mt + 8 i + 4 (l/32) + r, column 32 t + l % 32 of the wave's 64; direct
+  // stores would be 2-byte scatters. The tile goes through the two token
+  // buffers instead (free once every wave is past its last read), then out
+  // in full rows with 16-byte stores. Staged row R keeps its 16-byte unit u
+  // at u ^ (R % 16), so the accumulator-layout writes (rows 4 apart) and the
+  // row-major reads both fall in distinct banks.
+  __syncthreads();
+  if (p.split == 1) {
+    // bf16 tile: BM rows of 256 columns (512 bytes), rows 0..63 in s_a0
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt)
+    for (int mt = 0; mt < kLmMT; ++mt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int out = s_out[mt * 16 + kb * 4 + r];
-      if (out < 0) continue;
-      const float t = (p.split == 1 && p.mode == 0 && p.topk_w) ? p.topk_w[out] : 1.0f;
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const int ncol = (nt0 + nt) * 16 + col;
-        if (p.split > 1)
-          p.ws[((size_t)sp * p.rows_cap + out) * p.N + ncol] = acc[mt][nt][r];
-        else
-          p.c[(size_t)out * p.N + ncol] = (uint16_t)(cvt_pk_bf16(acc[mt][nt][r] * t, 0.f) & 0xFFFFu);
+        for (int r = 0; r < 4; ++r) {
+          const int R = mt * 32 + 8 * i + 4 * kq + r;
+          const int out = s_out[R];
+          const float tw = (p.mode == 0 && p.topk_w && out >= 0) ? p.topk_w[out] : 1.0f;
+          uint8_t* row = mt < kLmMT / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+#pragma unroll
+          for (int t = 0; t < kLmNT; ++t) {
+            const int C = w * 64 + t * 32 + l32;
+            *(uint16_t*)(row + (((C >> 3) ^ (R & 15)) << 4) + (C & 7) * 2) =
+                (uint16_t)(cvt_pk_bf16(acc[mt][t][4 * i + r] * tw, 0.f) & 0xFFFFu);
+          }
+        }
+    __syncthreads();
+    const int u = threadIdx.x & 31;
+#pragma unroll 4
+    for (int it = 0; it < BM / 8; ++it) {
+      const int R = it * 8 + (threadIdx.x >> 5);
+      const int out = s_out[R];
+      const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+      const u32x4 v = *(const u32x4*)(row + ((u ^ (R & 15)) << 4));
+      if (out >= 0) *(u32x4*)(p.c + (size_t)out * p.N + nb * kLmBN + u * 8) = v;
+    }
+  } else {
+    // fp32 partial sums: two passes of BM/2 rows of 256 columns (1 KiB)
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {
+      if (hp) __syncthreads();
+#pragma unroll
+      for (int mt = hp * kLmMT / 2; mt < (hp + 1) * kLmMT / 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int L = mt * 32 + 8 * i + 4 * kq + r - hp * BM / 2;
+            uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
+#pragma unroll
+            for (int t = 0; t < kLmNT; ++t) {
+              const int C = w * 64 + t * 32 + l32;
+              *(float*)(row + (((C >> 2) ^ (L & 15)) << 4) + (C & 3) * 4) = acc[mt][t][4 * i + r];
+            }
+          }
+      __syncthreads();
+      const int u = threadIdx.x & 63;
+#pragma unroll 4
+      for (int it = 0; it < BM / 8; ++it) {
+        const int L = it * 4 + (threadIdx.x >> 6);
+        const int out = s_out[hp * BM / 2 + L];
+        const uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
+        const u32x4 v = *(const u32x4*)(row + ((u ^ (L & 15)) << 4));
+        if (out >= 0)
+          *(u32x4*)(p.ws + ((size_t)sp * p.rows_cap + out) * p.N + nb * kLmBN + u * 4) = v;
       }
     }
-}
-
-template <int MT>
-static int launch_large_m_inst(const GemmParams& gp, unsigned grid, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_large_m_kernel<MT>), dim3(grid), dim3(256), 0, st, gp);
-  return (int)hipGetLastError();
+  }
 }
 
 template <int TM, int NTW, int WK, int D>
@@ -890,10 +980,10 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   if (grid <= 0) return 0;
   if (grid >= (1ll << 24)) return (int)hipErrorInvalidConfiguration;
   if (pl.kernel == QMA_KERNEL_LARGE_M) {
-    if ((pl.block_m != 128 && pl.block_m != 256) || pl.block_n != kLmBN || L.N % kLmBN != 0)
+    if (pl.block_m != kLmBM || pl.block_n != kLmBN || L.N % kLmBN != 0)
       return (int)hipErrorInvalidConfiguration;
-    int err = pl.block_m == 256 ? launch_large_m_inst<16>(gp, (unsigned)grid, st)
-                                : launch_large_m_inst<8>(gp, (unsigned)grid, st);
+    hipLaunchKernelGGL(gemm_large_m_kernel, dim3((unsigned)grid), dim3(256), 0, st, gp);
+    int err = (int)hipGetLastError();
     if (err == 0 && gp.split > 1) {
       const int64_t total = (int64_t)gp.num_tiles * gp.BM * (gp.N / 4);
       const unsigned rb = (unsigned)std::min<int64_t>((total + 255) / 256, 8192);

@@ -121,9 +121,28 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     assert q.split_k == 1 and q.block_n == 128
 
 
+def test_large_m_rule():
+    # indexed: large-M from 80 routed rows per expert, or on request
+    assert _plan(48, 4096, 7168, 48 * 80, 1).kernel == qma.KERNEL_LARGE_M
+    assert _plan(48, 4096, 7168, 48 * 79, 1).kernel == qma.KERNEL_SMALL_M
+    p = _plan(8, 256, 256, 64, 2, force=128)
+    assert p.kernel == qma.KERNEL_LARGE_M and p.block_m == 128 and p.block_n == 256
+    # contiguous: every 128-row tile holds one expert, so large-M whatever M/E
+    lay = qma.qma_layer_create(48, 4096, 7168, qma.PATH_GROUPED_CONTIGUOUS)
+    try:
+        for M in (128, 512, 6144):
+            q = qma.qma_plan_grouped(lay, M, 0)
+            assert q.kernel == qma.KERNEL_LARGE_M and q.block_m == 128, M
+    finally:
+        qma.qma_layer_destroy(lay)
+
+
 def test_plan_rejects_bad_force_and_wrong_path():
+    for bad in (48, 256):
+        with pytest.raises(qma.QmaError):
+            _plan(48, 4096, 7168, 576, 1, force=bad)
     with pytest.raises(qma.QmaError):
-        _plan(48, 4096, 7168, 576, 1, force=48)
+        _plan(8, 24 * 16, 256, 64, 2, force=128)             # N % 256 != 0
     lay = qma.qma_layer_create(8, 256, 256, qma.PATH_GROUPED_MASKED)
     try:
         with pytest.raises(qma.QmaError):
