@@ -116,7 +116,8 @@ typedef struct qma_plan {
   int32_t est_tiles;     /* M x N tiles expected without split-K */
   int32_t profile;       /* qma_profile */
   int32_t waves_k;       /* K partitions inside one workgroup */
-  int32_t reserved[2];
+  int32_t expected_m;    /* masked layers: the expected_m planned for, else 0 */
+  int32_t n_stream;      /* N blocks one workgroup streams through (>= 1) */
 } qma_plan_t;
 
 /* ---- layer (load time) ------------------------------------------------ */

@@ -106,6 +106,17 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   }
   p->split_k = split;
   p->k_depth = qma::small_m_depth(tm, ntw) * qma::kChunkK;
+  // Short K (a down projection of a narrow TP share): a workgroup that saw
+  // only one or two chunks would spend its life on start-up and one memory
+  // round trip. It streams several N blocks of its expert through the same
+  // load pipeline instead, as long as the grid keeps >= 4 workgroups per CU.
+  p->n_stream = 1;
+  if (wk == 1 && split == 1 && tm == 1 && ntw >= 2 && L.k_chunks < qma::kStreamChunks) {
+    const int32_t nblocks = L.N / p->block_n;
+    int32_t ns = std::min<int32_t>(ceil_div(qma::kStreamChunks, (int32_t)L.k_chunks), nblocks);
+    while (ns > 1 && (int64_t)tiles_m * ceil_div(nblocks, ns) < 4 * qma::kNumCUs) --ns;
+    p->n_stream = std::max<int32_t>(ns, 1);
+  }
 }
 
 // Large-M kernel: 128-token tiles, 256 columns per workgroup.
@@ -136,6 +147,7 @@ void plan_common(const Layer& L, qma_plan_t* p) {
   p->k = L.K;
   p->profile = L.profile;
   p->split_k = 1;
+  p->n_stream = 1;
 }
 
 // Activations are addressed with 32-bit buffer offsets.
@@ -166,6 +178,10 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
   if (plan->split_k < 1 || plan->split_k > 8)
     return fail(QMA_ERR_INVALID_ARG, "plan has bad split_k %d", plan->split_k);
+  if (plan->n_stream < 1 || plan->n_stream > 64 ||
+      (plan->n_stream > 1 && (plan->kernel != QMA_KERNEL_SMALL_M || plan->waves_k != 1 ||
+                              plan->split_k != 1 || plan->block_m != 16)))
+    return fail(QMA_ERR_INVALID_ARG, "plan has bad n_stream %d", plan->n_stream);
   if (plan->block_n != 16 && plan->block_n != 32 && plan->block_n != 64 &&
       plan->block_n != 128 && plan->block_n != 256)
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_n %d", plan->block_n);
@@ -344,7 +360,7 @@ qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
     out->tok_e_x100 = expected_m * 100;
     const int32_t bm = expected_m <= 16 ? 16 : (expected_m <= 32 ? 32 : 64);
     plan_small_m(L, bm, L.E * std::max(1, ceil_div(std::max(expected_m, 1), bm)), out);
-    out->reserved[0] = expected_m;
+    out->expected_m = expected_m;
     return ok();
   }
   return fail(QMA_ERR_INVALID_ARG, "layer is not a grouped layer");
@@ -550,9 +566,9 @@ qma_status qma_grouped_masked_gemm(const qma_layer_t* layer, const qma_plan_t* p
   if (s != QMA_OK) return s;
   if (Mb < 1 || (int64_t)Mb * layer->L.E != plan->rows)
     return fail(QMA_ERR_INVALID_ARG, "budget %d does not match the plan", Mb);
-  if (expected_m != plan->reserved[0])
+  if (expected_m != plan->expected_m)
     return fail(QMA_ERR_INVALID_ARG, "expected_m %d does not match the plan's %d", expected_m,
-                plan->reserved[0]);
+                plan->expected_m);
   if (!a || !masked_m || !packed_w || !c) return fail(QMA_ERR_INVALID_ARG, "null buffer");
   if (!aligned(a, 16) || !aligned(c, 16) || !aligned(packed_w, 256))
     return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");

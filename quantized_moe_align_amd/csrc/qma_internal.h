@@ -24,6 +24,8 @@ constexpr int kWBlockBytes = 1024;
 constexpr int kSBlockBytes = 128;
 constexpr int kMaxExperts = 1024;  // moe_align's single-workgroup limit
 constexpr int kNumCUs = 256;
+// chunks a streaming small-M workgroup aims to keep in its load pipeline
+constexpr int kStreamChunks = 8;
 
 struct Layer {
   int32_t E, N, K;

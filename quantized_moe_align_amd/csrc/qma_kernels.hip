@@ -262,6 +262,7 @@ struct GemmParams {
   int32_t mode, a_row_div, num_tiles, nblocks, split, num_slots;
   int32_t Mb, tiles_per_expert, rows_cap, cap;
   int32_t E, N, K, NT, KC, BM;
+  int32_t nstream, nbtot;  // streaming small-M: N blocks per workgroup, N blocks in all
 };
 
 struct RowInfo {
@@ -544,6 +545,150 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
 // splits summed in order ([release] indexed techniques: the split/reduce
 // that the stream-K gate avoids on saturated grids). One thread per
 // (row position, 4 columns).
+// Streaming small-M variant for short K: one 16-token tile, the four waves
+// side by side over 64 * NTW / 4 ... columns as in the kernel above (one K
+// partition), but a workgroup walks p.nstream consecutive column blocks of
+// its expert. The (column block, K chunk) pairs form one stream through the
+// D-stage load pipeline, so the next block's weights are in flight while the
+// current block finishes, and a block's outputs are stored as soon as its
+// last chunk is accumulated. Token rows, output rows and topk weights are
+// looked up once per workgroup.
+template <int NTW, int D>
+__global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmParams p) {
+  int tile, grp, sp;
+  if (!decode_bid(p, tile, grp, sp)) return;
+  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
+  if (e < 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int col = lane & 15, kb = lane >> 4;
+  const int KC = p.KC;
+  const int nb0 = grp * p.nstream;
+  const int total = min(p.nstream, p.nbtot - nb0) * KC;
+
+  // Weights of the whole expert; this wave's tiles of column block nb are
+  // (nb * 4 + w) * NTW + nt.
+  const uint32_t tile_bytes = (uint32_t)KC * kWBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(p.wpk + (size_t)e * p.NT * tile_bytes, (uint32_t)p.NT * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.spk + (size_t)e * p.NT * KC * kSBlockBytes, (uint32_t)p.NT * KC * kSBlockBytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
+  const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
+  const RowInfo rx = row_info(p, tile, e, col);
+  const uint32_t voff_x = rx.valid ? (uint32_t)rx.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
+  int32_t out_row[4];
+  float tw[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const RowInfo ri = row_info(p, tile, e, kb * 4 + r);
+    out_row[r] = ri.valid ? ri.out_row : -1;
+    tw[r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+  }
+
+  struct Stage {
+    u32x4 w[NTW];
+    u32x2 s[NTW];
+    u32x4 x[4];
+  };
+  Stage st[D];
+  // load cursor: column block and chunk of the next stage to fetch
+  int l_nb = nb0, l_c = 0;
+  auto load_next = [&](Stage& s) {
+    const int t0 = l_nb * 4 * NTW;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, voff_w, (t0 + nt) * tile_bytes + l_c * kWBlockBytes, kNonTemporal);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
+                                                     ((t0 + nt) * KC + l_c) * kSBlockBytes, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
+    if (++l_c == KC) {
+      l_c = 0;
+      ++l_nb;
+    }
+  };
+
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // compute cursor: column block and chunk of the next stage to consume
+  int c_nb = nb0, c_c = 0;
+  auto step = [&](const Stage& s) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 xs = mfma16(s.x[g], neg136, zero4);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const u32x4 wb = unpack_128q(s.w[nt][g]);
+        const uint32_t sw = s.s[nt][g >> 1];
+        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        const f32x4 pr = mfma16(s.x[g], wb, xs);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
+      }
+    }
+    if (++c_c == KC) {
+      // column block c_nb complete: lane holds rows 4*kb + r of column col
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (out_row[r] >= 0)
+            p.c[(size_t)out_row[r] * p.N + n] =
+                (uint16_t)(pack_bf16x2(acc[nt][r] * tw[r], 0.f) & 0xFFFFu);
+          acc[nt][r] = 0.f;
+        }
+      }
+      c_c = 0;
+      ++c_nb;
+    }
+  };
+
+  // Same pipeline as the kernel above, over the flattened stream.
+  int f = 0;
+  if (total >= 2 * D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_next(st[d]);
+    }
+    for (; f + 2 * D <= total; f += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        __builtin_amdgcn_sched_barrier(0);
+        step(st[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(st[d]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < total) load_next(st[d]);
+  }
+  for (; f < total; f += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (f + d < total) {
+        step(st[d]);
+        if (f + d + D < total) load_next(st[d]);
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
   const int64_t per_row = p.N / 4;
   const int64_t total = (int64_t)p.num_tiles * p.BM * per_row;
@@ -996,6 +1141,22 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
   const int depth = pl.k_depth / kChunkK;
+  if (pl.n_stream > 1) {
+    if (tm != 1 || wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) ||
+        ntw * 64 != pl.block_n)
+      return (int)hipErrorInvalidConfiguration;
+    gp.nstream = pl.n_stream;
+    gp.nbtot = gp.nblocks;
+    gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
+    const int64_t sgrid = tiles_pad * gp.nblocks;
+    if (ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), dim3((unsigned)sgrid), dim3(256), 0, st,
+                         gp);
+    else
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), dim3((unsigned)sgrid), dim3(256), 0, st,
+                         gp);
+    return (int)hipGetLastError();
+  }
   if (!small_m_supported(tm, ntw) || (wk != 1 && wk != 2 && wk != 4) ||
       ntw * 16 * (4 / wk) != pl.block_n)
     return (int)hipErrorInvalidConfiguration;

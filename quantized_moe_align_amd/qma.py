@@ -59,10 +59,10 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "path", "kernel", "block_m", "block_n", "split_k", "k_depth",
         "num_experts", "n", "k", "rows", "tok_e_x100", "est_tiles", "profile",
-        "waves_k")] + [("reserved", ctypes.c_int32 * 2)]
+        "waves_k", "expected_m", "n_stream")]
 
     def as_dict(self):
-        return {n: getattr(self, n) for n, _ in self._fields_ if n != "reserved"}
+        return {n: getattr(self, n) for n, _ in self._fields_}
 
 
 _lib = None

@@ -401,3 +401,63 @@ def test_graph_capture_replays_match_eager(gpu):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
+
+
+# Streaming small-M (one workgroup walks several column blocks of its
+# expert): (E, T, topk, K, N, block_n, n_stream). 7 or 14 column blocks, so
+# some streams end on a partial group.
+STREAM_CASES = [
+    (5, 40, 2, 256, 1792, 256, 3),
+    (5, 40, 2, 256, 1792, 256, 7),
+    (3, 30, 1, 128, 1792, 128, 4),
+    (4, 24, 3, 384, 512, 128, 2),
+]
+
+
+def _stream_override(block_n, n_stream):
+    return {"kernel": qma.KERNEL_SMALL_M, "block_m": 16, "block_n": block_n, "waves_k": 1,
+            "split_k": 1, "n_stream": n_stream}
+
+
+@pytest.mark.parametrize("case", STREAM_CASES)
+def test_stream_integer_exact_bitwise(gpu, case):
+    E, T, topk, K, N, bn, ns = case
+    rng = np.random.default_rng(80 + ns)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=16, override=_stream_override(bn, ns))
+    assert plan.n_stream == ns
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(got[valid], rne(ref[valid]))
+    assert np.all(got[~valid] == SENT)
+    one, _ = indexed(a, topk, ids, w, s, force_bm=16, override=_stream_override(bn, 1))
+    assert np.array_equal(one, got)
+
+
+def test_stream_random_topk_weights_and_grouped(gpu):
+    E, T, topk, K, N = 6, 50, 2, 256, 1024
+    rng = np.random.default_rng(90)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    tw = rng.random(T * topk).astype(np.float32)
+    got, _ = indexed(a, topk, ids, w, s, force_bm=16, topk_w=tw, override=_stream_override(256, 3))
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s, topk_weights=tw)
+    assert_per_expert(got, ref, slot_experts(ids, E), "stream indexed")
+    # contiguous and masked routing through the streaming kernel
+    wl = inputs.make_contiguous("c", 5, E, 0, K, N // 2, counts=[20, 0, 7, 16, 1, 33],
+                                weights=False)
+    m_idx = wl["m_indices"]
+    got_c = contiguous(wl["a"], m_idx, w, s, _stream_override(256, 2))
+    assert_per_expert(got_c, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx, "stream contiguous")
+    Mb = 32
+    masked_m = np.array([16, 0, 32, 1, 9, 17], np.int32)
+    am = inputs.bf16_normal(rng, (E, Mb, K))
+    got_m = masked(am, masked_m, 16, w, s, _stream_override(128, 4))
+    ref_m = O.grouped_masked(am, masked_m, w, s)
+    row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
+    assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N), row_e.reshape(-1),
+                      "stream masked")
+    assert np.all(got_m[row_e < 0] == SENT)

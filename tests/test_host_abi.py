@@ -121,6 +121,17 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     assert q.split_k == 1 and q.block_n == 128
 
 
+def test_stream_rule():
+    # TP8 down share: K = 256 is two chunks, so a workgroup streams 4 column
+    # blocks (8 chunks) and the grid keeps >= 4 workgroups per CU
+    d = _plan(384, 7168, 256, 256, 8)
+    assert d.kernel == qma.KERNEL_SMALL_M and d.waves_k == 1 and d.split_k == 1
+    assert d.n_stream == 4
+    assert _plan(48, 7168, 2048, 558, 1).n_stream == 1      # EP8 down: K long enough
+    assert _plan(48, 4096, 7168, 558, 1).n_stream == 1      # K split across waves
+    assert _plan(8, 256, 128, 64, 2).n_stream == 1          # grid too small to stream
+
+
 def test_large_m_rule():
     # indexed: large-M from 80 routed rows per expert, or on request
     assert _plan(48, 4096, 7168, 48 * 80, 1).kernel == qma.KERNEL_LARGE_M
