@@ -79,7 +79,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   const int tm = bm / 16;
   // The four waves of a workgroup split K in two when K is long (each wave
   // still streams >= 12 chunks of 128) and split the columns otherwise.
-  int wk = L.k_chunks >= 24 ? 2 : 1;
+  // 32-row tiles keep one K partition: their kernel stages token rows in
+  // per-wave LDS buffers, which fits the register budget only that way.
+  int wk = (tm == 1 && L.k_chunks >= 24) ? 2 : 1;
   if (L.N % (16 * (4 / wk)) != 0) wk = 4;
   const int wn = 4 / wk;
   int ntw = 0;
@@ -105,7 +107,8 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     split = std::max<int32_t>(split, 1);
   }
   p->split_k = split;
-  p->k_depth = qma::small_m_depth(tm, ntw) * qma::kChunkK;
+  p->k_depth = (tm == 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw)) *
+               qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
   // only one or two chunks would spend its life on start-up and one memory
   // round trip. It streams several N blocks of its expert through the same

@@ -26,6 +26,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
+// Calls f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <int N, typename F, int I = 0>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, F, I + 1>(static_cast<F&&>(f));
+  }
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); }
 
@@ -349,6 +358,38 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            kBufWord3);
 }
 
+// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS byte address of a __shared__ object.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Reads of LDS filled by direct-to-LDS loads are issued as ds_read_b128 in
+// inline asm and waited with explicit counts (wait_lgkm ties the wait to the
+// register it guards, so the consumer cannot move above it). The compiler
+// then tracks no such read: its own wait counts for direct-to-LDS loads turn
+// conservative where control flow merges and would wait for every
+// prefetch. LDS operations complete in order, so these reads can only make
+// the compiler's own counts stricter.
+template <int OFF>
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(v) : "v"(addr), "n"(OFF) : "memory");
+  return v;
+}
+
+template <int N>
+__device__ __forceinline__ void wait_lgkm(u32x4& v) {
+  static_assert(N >= 0 && N < 16, "lgkmcnt range");
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
+}
+
 // Decode the XCD-aware workgroup order. Workgroup i runs on XCD i % 8, and
 // XCD x takes token tiles x, x+8, ... with all of their (column block,
 // split) pieces. A tile's activations then stay in one XCD's L2, and empty
@@ -545,16 +586,24 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
 // splits summed in order ([release] indexed techniques: the split/reduce
 // that the stream-K gate avoids on saturated grids). One thread per
 // (row position, 4 columns).
-// Streaming small-M variant for short K: one 16-token tile, the four waves
-// side by side over 64 * NTW / 4 ... columns as in the kernel above (one K
-// partition), but a workgroup walks p.nstream consecutive column blocks of
-// its expert. The (column block, K chunk) pairs form one stream through the
-// D-stage load pipeline, so the next block's weights are in flight while the
-// current block finishes, and a block's outputs are stored as soon as its
-// last chunk is accumulated. Token rows, output rows and topk weights are
-// looked up once per workgroup.
-template <int NTW, int D>
+// Small-M variant with one K partition per workgroup: TM 16-token tiles,
+// the four waves side by side over 16 * NTW columns each. A workgroup walks
+// p.nstream consecutive column blocks of its expert (one block unless the
+// plan streams): the (column block, K chunk) pairs form one stream through
+// the D-stage load pipeline, so the next block's weights are in flight while
+// the current block finishes, and a block's outputs are stored as soon as its
+// last chunk is accumulated. With XL the token rows go through LDS instead
+// of registers: each wave copies its chunk's rows with direct-to-LDS loads
+// into a private buffer per stage (slot j of row r holds segment
+// j ^ (r % 16), so an operand read hits 16 distinct banks), which keeps a
+// 32-token tile's pipeline inside the register budget.
+template <int TM, int NTW, int D, bool XL>
 __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmParams p) {
+  constexpr int XROW = 256;                  // bytes of one row's 128-wide chunk
+  constexpr int XBUF = TM * 16 * XROW;       // one stage of one wave
+  constexpr int NXL = TM * 4;                // direct-to-LDS loads per stage (4 rows each)
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[XL ? 4 * D * XBUF : 16];
+
   int tile, grp, sp;
   if (!decode_bid(p, tile, grp, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
@@ -577,26 +626,44 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
   const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
   const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
-  const RowInfo rx = row_info(p, tile, e, col);
-  const uint32_t voff_x = rx.valid ? (uint32_t)rx.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
-  int32_t out_row[4];
-  float tw[4];
+  // token rows: registers (lane = column of the operand) or LDS copies
+  uint32_t voff_x[XL ? NXL : TM];
+  if constexpr (XL) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const RowInfo ri = row_info(p, tile, e, kb * 4 + r);
-    out_row[r] = ri.valid ? ri.out_row : -1;
-    tw[r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+    for (int i = 0; i < NXL; ++i) {
+      const int row = 4 * i + kb;
+      const RowInfo ri = row_info(p, tile, e, row);
+      const uint32_t seg = (uint32_t)(col ^ (row & 15));
+      voff_x[i] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
+    }
+  } else {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const RowInfo ri = row_info(p, tile, e, tm * 16 + col);
+      voff_x[tm] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
+    }
   }
+  int32_t out_row[TM][4];
+  float tw[TM][4];
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const RowInfo ri = row_info(p, tile, e, tm * 16 + kb * 4 + r);
+      out_row[tm][r] = ri.valid ? ri.out_row : -1;
+      tw[tm][r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+    }
 
   struct Stage {
     u32x4 w[NTW];
     u32x2 s[NTW];
-    u32x4 x[4];
+    u32x4 x[XL ? 1 : TM][4];
   };
   Stage st[D];
   // load cursor: column block and chunk of the next stage to fetch
   int l_nb = nb0, l_c = 0;
-  auto load_next = [&](Stage& s) {
+  auto load_next = [&](Stage& s, auto d_id) {
+    constexpr int d = decltype(d_id)::value;
     const int t0 = l_nb * 4 * NTW;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
@@ -606,86 +673,133 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
     for (int nt = 0; nt < NTW; ++nt)
       s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
                                                      ((t0 + nt) * KC + l_c) * kSBlockBytes, 0);
+    if constexpr (XL) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
+      for (int i = 0; i < NXL; ++i) {
+        const int vo = (int)voff_x[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ra, (__attribute__((address_space(3))) void*)(s_x + (w * D + d) * XBUF + 4 * i * XROW),
+            16, vo, l_c * XROW, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          s.x[tm][g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x[tm] + g * 64, l_c * XROW, 0);
+    }
     if (++l_c == KC) {
       l_c = 0;
       ++l_nb;
     }
   };
 
-  f32x4 acc[NTW];
+  f32x4 acc[NTW][TM];
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // LDS operand reads: lane l takes row tm*16 + l%16, segment 4g + l/16,
+  // stored at slot segment ^ (l % 16); tiles differ by 16 rows (offset).
+  const uint32_t xrd = lds_addr(s_x) + (uint32_t)(w * D) * XBUF + col * XROW;
 
   // compute cursor: column block and chunk of the next stage to consume
   int c_nb = nb0, c_c = 0;
-  auto step = [&](const Stage& s) {
+  auto step = [&](const Stage& s, auto d_id, auto tail) {
+    constexpr int d = decltype(d_id)::value;
+    if constexpr (XL) {
+      // this stage's token rows: in the steady loop D - 1 later stages'
+      // loads were issued after them; in the tail the count varies
+      if constexpr (decltype(tail)::value)
+        wait_vmcnt<0>();
+      else
+        wait_vmcnt<(D - 1) * (2 * NTW + NXL)>();
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const f32x4 xs = mfma16(s.x[g], neg136, zero4);
+      u32x4 xg[TM];
+      if constexpr (XL) {
+        const uint32_t a = xrd + d * XBUF + (((4 * g + kb) ^ col) << 4);
+        xg[0] = lds_read16<0>(a);
+        if constexpr (TM > 1) xg[1] = lds_read16<16 * XROW>(a);
+        if constexpr (TM > 1) {
+          wait_lgkm<1>(xg[0]);
+          wait_lgkm<0>(xg[1]);
+        } else {
+          wait_lgkm<0>(xg[0]);
+        }
+      } else {
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) xg[tm] = s.x[tm][g];
+      }
+      f32x4 xs[TM];
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) xs[tm] = mfma16(xg[tm], neg136, zero4);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const u32x4 wb = unpack_128q(s.w[nt][g]);
         const uint32_t sw = s.s[nt][g >> 1];
         const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        const f32x4 pr = mfma16(s.x[g], wb, xs);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
+        for (int tm = 0; tm < TM; ++tm) {
+          const f32x4 pr = mfma16(xg[tm], wb, xs[tm]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][tm][r] = __builtin_fmaf(scv, pr[r], acc[nt][tm][r]);
+        }
       }
     }
     if (++c_c == KC) {
-      // column block c_nb complete: lane holds rows 4*kb + r of column col
+      // column block c_nb complete: lane holds rows tm*16 + 4*kb + r, column col
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (out_row[r] >= 0)
-            p.c[(size_t)out_row[r] * p.N + n] =
-                (uint16_t)(pack_bf16x2(acc[nt][r] * tw[r], 0.f) & 0xFFFFu);
-          acc[nt][r] = 0.f;
-        }
+        for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            if (out_row[tm][r] >= 0)
+              p.c[(size_t)out_row[tm][r] * p.N + n] =
+                  (uint16_t)(pack_bf16x2(acc[nt][tm][r] * tw[tm][r], 0.f) & 0xFFFFu);
+            acc[nt][tm][r] = 0.f;
+          }
       }
       c_c = 0;
       ++c_nb;
     }
   };
+  using Loop = std::false_type;
+  using Tail = std::true_type;
 
   // Same pipeline as the kernel above, over the flattened stream.
   int f = 0;
   if (total >= 2 * D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
+    static_for<D>([&](auto d) {
       __builtin_amdgcn_sched_barrier(0);
-      load_next(st[d]);
-    }
+      load_next(st[d], d);
+    });
     for (; f + 2 * D <= total; f += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
+      static_for<D>([&](auto d) {
         __builtin_amdgcn_sched_barrier(0);
-        step(st[d]);
+        step(st[d], d, Loop{});
         __builtin_amdgcn_sched_barrier(0);
-        load_next(st[d]);
-      }
+        load_next(st[d], d);
+      });
     }
     __builtin_amdgcn_sched_barrier(0);
   } else {
-#pragma unroll
-    for (int d = 0; d < D; ++d)
-      if (d < total) load_next(st[d]);
+    static_for<D>([&](auto d) {
+      if (d < total) load_next(st[d], d);
+    });
   }
   for (; f < total; f += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
+    static_for<D>([&](auto d) {
       if (f + d < total) {
-        step(st[d]);
-        if (f + d + D < total) load_next(st[d]);
+        step(st[d], d, Tail{});
+        if (f + d + D < total) load_next(st[d], d);
       }
-    }
+    });
   }
 }
 
@@ -783,13 +897,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
                cvt_pk_bf16(__builtin_fmaf(q23.x, s, neg8s), __builtin_fmaf(q23.y, s, neg8s)),
                cvt_pk_bf16(__builtin_fmaf(q45.x, s, neg8s), __builtin_fmaf(q45.y, s, neg8s)),
                cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
-}
-
-// s_waitcnt with only the vector-memory count constrained (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
 // Bare workgroup barrier. __syncthreads() also fences memory, and that
@@ -1141,20 +1248,25 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
   const int depth = pl.k_depth / kChunkK;
-  if (pl.n_stream > 1) {
-    if (tm != 1 || wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) ||
-        ntw * 64 != pl.block_n)
+  const bool xl = tm == 2 && wk == 1 && gp.split == 1 && (ntw == 2 || ntw == 4);
+  if (pl.n_stream > 1 || xl) {
+    // one K partition: the streaming kernel (16-row tiles streaming column
+    // blocks, or 32-row tiles with token rows staged in LDS)
+    if (wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) || ntw * 64 != pl.block_n ||
+        (tm != 1 && tm != 2))
       return (int)hipErrorInvalidConfiguration;
     gp.nstream = pl.n_stream;
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
-    const int64_t sgrid = tiles_pad * gp.nblocks;
-    if (ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), dim3((unsigned)sgrid), dim3(256), 0, st,
-                         gp);
+    const dim3 sg((unsigned)(tiles_pad * gp.nblocks));
+    if (tm == 1 && ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<1, 4, 4, false>), sg, dim3(256), 0, st, gp);
+    else if (tm == 1)
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<1, 2, 4, false>), sg, dim3(256), 0, st, gp);
+    else if (ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4, 2, true>), sg, dim3(256), 0, st, gp);
     else
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), dim3((unsigned)sgrid), dim3(256), 0, st,
-                         gp);
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 2, 2, true>), sg, dim3(256), 0, st, gp);
     return (int)hipGetLastError();
   }
   if (!small_m_supported(tm, ntw) || (wk != 1 && wk != 2 && wk != 4) ||

@@ -82,7 +82,8 @@ def test_indexed_random_within_tolerance(gpu, shape, force_bm):
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("force_bm,ntw,wk", [(0, 0, 0), (16, 1, 4), (16, 2, 1), (16, 4, 2),
                                              (16, 4, 4), (16, 4, 1), (32, 4, 4), (32, 2, 2),
-                                             (32, 1, 1), (64, 2, 4), (64, 1, 2)])
+                                             (32, 1, 1), (32, 4, 1), (32, 2, 1), (64, 2, 4),
+                                             (64, 1, 2)])
 def test_indexed_integer_exact_bitwise(gpu, shape, force_bm, ntw, wk):
     E, T, topk, K, N = shape
     block_n = ntw * 16 * (4 // wk) if ntw else 0
