@@ -407,6 +407,36 @@ __device__ __forceinline__ bool decode_bid(const GemmParams& p, int& tile, int& 
   return tile < p.num_tiles;
 }
 
+// Workgroup order of the large-M kernel. A token tile is read by every
+// column block, and a weight slice (256 columns of one expert) by every
+// token tile of the expert. The work items (token tile, column block,
+// split) are listed tile by tile (in groups of kLmGroup tiles sharing a
+// column block when that is > 1), and XCD x walks the x-th eighth of the
+// list in order: a tile's column blocks run together on one XCD, and so do
+// the same column block of an expert's consecutive tiles, so both stay in
+// that XCD's L2. The list covers only tiles that hold rows (the routed
+// count is read on the device), so every XCD gets an equal share of work.
+constexpr int kLmGroup = 1;
+__device__ __forceinline__ bool decode_bid_lm(const GemmParams& p, int& tile, int& nb, int& sp) {
+  const int ntiles = p.mode == 0 ? min(*p.ntp / p.BM, p.num_tiles) : p.num_tiles;
+  const int per = p.nblocks * p.split;
+  const int items = ntiles * per;
+  const int chunk = (items + 7) >> 3;
+  const int bid = blockIdx.x;
+  const int j = bid >> 3;
+  if (j >= chunk) return false;
+  const int i = (bid & 7) * chunk + j;
+  if (i >= items) return false;
+  const int s = i / (kLmGroup * per);
+  const int rem = i - s * kLmGroup * per;
+  const int g = min(kLmGroup, ntiles - s * kLmGroup);
+  const int nbsp = rem / g;
+  tile = s * kLmGroup + (rem - nbsp * g);
+  nb = nbsp / p.split;
+  sp = nbsp - nb * p.split;
+  return true;
+}
+
 template <int TM, int NTW, int WK, int D>
 __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p) {
   constexpr int WN = 4 / WK;
@@ -922,7 +952,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
   __shared__ int32_t s_out[BM];
 
   int tile, nb, sp;
-  if (!decode_bid(p, tile, nb, sp)) return;
+  if (!decode_bid_lm(p, tile, nb, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
   if (e < 0) return;
   const int lane = threadIdx.x & 63;
@@ -997,7 +1027,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         b.w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(
-            rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, kNonTemporal);
+            rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, 0);
 #pragma unroll
     for (int t = 0; t < kLmNT; ++t)
       b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
