@@ -384,6 +384,17 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   return v;
 }
 
+// Bare workgroup barrier. __syncthreads() also fences memory, and that
+// fence waits for every outstanding direct-to-LDS load, including prefetches
+// of later chunks. The kernels that use this wait with explicit vmcnt
+// counts, and the asm clobbers keep the compiler from moving memory
+// operations across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_lgkm(u32x4& v) {
   static_assert(N >= 0 && N < 16, "lgkmcnt range");
@@ -616,24 +627,16 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
 // splits summed in order ([release] indexed techniques: the split/reduce
 // that the stream-K gate avoids on saturated grids). One thread per
 // (row position, 4 columns).
-// Small-M variant with one K partition per workgroup: TM 16-token tiles,
-// the four waves side by side over 16 * NTW columns each. A workgroup walks
-// p.nstream consecutive column blocks of its expert (one block unless the
-// plan streams): the (column block, K chunk) pairs form one stream through
-// the D-stage load pipeline, so the next block's weights are in flight while
-// the current block finishes, and a block's outputs are stored as soon as its
-// last chunk is accumulated. With XL the token rows go through LDS instead
-// of registers: each wave copies its chunk's rows with direct-to-LDS loads
-// into a private buffer per stage (slot j of row r holds segment
-// j ^ (r % 16), so an operand read hits 16 distinct banks), which keeps a
-// 32-token tile's pipeline inside the register budget.
-template <int TM, int NTW, int D, bool XL>
+// Streaming small-M variant for short K: one 16-token tile, one K
+// partition, the four waves side by side over 16 * NTW columns each. A
+// workgroup walks p.nstream consecutive column blocks of its expert: the
+// (column block, K chunk) pairs form one stream through the D-stage load
+// pipeline, so the next block's weights are in flight while the current
+// block finishes, and a block's outputs are stored as soon as its last
+// chunk is accumulated. Token rows, output rows and topk weights are looked
+// up once per workgroup.
+template <int NTW, int D>
 __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmParams p) {
-  constexpr int XROW = 256;                  // bytes of one row's 128-wide chunk
-  constexpr int XBUF = TM * 16 * XROW;       // one stage of one wave
-  constexpr int NXL = TM * 4;                // direct-to-LDS loads per stage (4 rows each)
-  __shared__ __attribute__((aligned(1024))) uint8_t s_x[XL ? 4 * D * XBUF : 16];
-
   int tile, grp, sp;
   if (!decode_bid(p, tile, grp, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
@@ -656,22 +659,167 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
   const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
   const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
-  // token rows: registers (lane = column of the operand) or LDS copies
-  uint32_t voff_x[XL ? NXL : TM];
-  if constexpr (XL) {
+  const RowInfo rx = row_info(p, tile, e, col);
+  const uint32_t voff_x = rx.valid ? (uint32_t)rx.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
+  int32_t out_row[4];
+  float tw[4];
 #pragma unroll
-    for (int i = 0; i < NXL; ++i) {
-      const int row = 4 * i + kb;
-      const RowInfo ri = row_info(p, tile, e, row);
-      const uint32_t seg = (uint32_t)(col ^ (row & 15));
-      voff_x[i] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
+  for (int r = 0; r < 4; ++r) {
+    const RowInfo ri = row_info(p, tile, e, kb * 4 + r);
+    out_row[r] = ri.valid ? ri.out_row : -1;
+    tw[r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+  }
+
+  struct Stage {
+    u32x4 w[NTW];
+    u32x2 s[NTW];
+    u32x4 x[4];
+  };
+  Stage st[D];
+  // load cursor: column block and chunk of the next stage to fetch
+  int l_nb = nb0, l_c = 0;
+  auto load_next = [&](Stage& s) {
+    const int t0 = l_nb * 4 * NTW;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, voff_w, (t0 + nt) * tile_bytes + l_c * kWBlockBytes, kNonTemporal);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
+                                                     ((t0 + nt) * KC + l_c) * kSBlockBytes, 0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
+    if (++l_c == KC) {
+      l_c = 0;
+      ++l_nb;
     }
+  };
+
+  f32x4 acc[NTW];
+#pragma unroll
+  for (int nt = 0; nt < NTW; ++nt) acc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+
+  // compute cursor: column block and chunk of the next stage to consume
+  int c_nb = nb0, c_c = 0;
+  auto step = [&](const Stage& s) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const f32x4 xs = mfma16(s.x[g], neg136, zero4);
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const u32x4 wb = unpack_128q(s.w[nt][g]);
+        const uint32_t sw = s.s[nt][g >> 1];
+        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        const f32x4 pr = mfma16(s.x[g], wb, xs);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
+      }
+    }
+    if (++c_c == KC) {
+      // column block c_nb complete: lane holds rows 4*kb + r of column col
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (out_row[r] >= 0)
+            p.c[(size_t)out_row[r] * p.N + n] =
+                (uint16_t)(pack_bf16x2(acc[nt][r] * tw[r], 0.f) & 0xFFFFu);
+          acc[nt][r] = 0.f;
+        }
+      }
+      c_c = 0;
+      ++c_nb;
+    }
+  };
+
+  // Same pipeline as the kernel above, over the flattened stream.
+  int f = 0;
+  if (total >= 2 * D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_next(st[d]);
+    }
+    for (; f + 2 * D <= total; f += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        __builtin_amdgcn_sched_barrier(0);
+        step(st[d]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_next(st[d]);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   } else {
 #pragma unroll
-    for (int tm = 0; tm < TM; ++tm) {
-      const RowInfo ri = row_info(p, tile, e, tm * 16 + col);
-      voff_x[tm] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
+    for (int d = 0; d < D; ++d)
+      if (d < total) load_next(st[d]);
+  }
+  for (; f < total; f += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (f + d < total) {
+        step(st[d]);
+        if (f + d + D < total) load_next(st[d]);
+      }
     }
+  }
+}
+
+// Small-M variant with the token rows shared by the workgroup: TM 16-token
+// tiles, one K partition, the four waves side by side over 16 * NTW columns
+// each, n_stream column blocks streamed as in the kernel above. A chunk's
+// token rows (TM * 16 rows x 256 bytes) go through a ring of D LDS buffers,
+// each wave copying a quarter of them with direct-to-LDS loads (slot j of
+// row r holds segment j ^ (r % 16)); weights go through D register stages
+// per wave. One bare barrier per chunk: at step j every wave has its own
+// loads of chunk j (wait count) and, past the barrier, every wave is done
+// with chunk j-1, whose buffer then takes chunk j+D-1. Sharing the rows
+// keeps the LDS (D * TM * 4 KiB) and register budget small enough for three
+// workgroups per CU, which the 32-token tiles of a masked decode need to keep
+// HBM busy, and loads each row once per workgroup instead of once per wave.
+template <int TM, int NTW, int D>
+__global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParams p) {
+  constexpr int XROW = 256;
+  constexpr int XBUF = TM * 16 * XROW;       // one chunk of the tile's token rows
+  constexpr int NX = TM;                     // direct-to-LDS loads per wave and chunk
+  constexpr int NW = 2 * NTW;                // weight + scale loads per wave and chunk
+  static_assert(D >= 2, "pipeline depth");
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[D * XBUF];
+
+  int tile, grp, sp;
+  if (!decode_bid(p, tile, grp, sp)) return;
+  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
+  if (e < 0) return;
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int col = lane & 15, kb = lane >> 4;
+  const int KC = p.KC;
+  const int nb0 = grp * p.nstream;
+  const int total = min(p.nstream, p.nbtot - nb0) * KC;
+
+  const uint32_t tile_bytes = (uint32_t)KC * kWBlockBytes;
+  const __amdgpu_buffer_rsrc_t rw =
+      make_rsrc(p.wpk + (size_t)e * p.NT * tile_bytes, (uint32_t)p.NT * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(p.spk + (size_t)e * p.NT * KC * kSBlockBytes, (uint32_t)p.NT * KC * kSBlockBytes);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
+  const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
+  // wave w copies rows 4 (w * NX + i) + l / 16, i < NX
+  uint32_t voff_x[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int row = 4 * (w * NX + i) + kb;
+    const RowInfo ri = row_info(p, tile, e, row);
+    const uint32_t seg = (uint32_t)(col ^ (row & 15));
+    voff_x[i] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
   int32_t out_row[TM][4];
   float tw[TM][4];
@@ -684,43 +832,42 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
       tw[tm][r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
     }
 
-  struct Stage {
+  // stream position f -> (column block, chunk); past the end the last
+  // chunk is fetched again, so every step issues the same loads
+  auto pos = [&](int f, int& nb, int& c) {
+    f = min(f, total - 1);
+    const int q = f / KC;
+    nb = nb0 + q;
+    c = f - q * KC;
+  };
+  struct WStage {
     u32x4 w[NTW];
     u32x2 s[NTW];
-    u32x4 x[XL ? 1 : TM][4];
   };
-  Stage st[D];
-  // load cursor: column block and chunk of the next stage to fetch
-  int l_nb = nb0, l_c = 0;
-  auto load_next = [&](Stage& s, auto d_id) {
-    constexpr int d = decltype(d_id)::value;
-    const int t0 = l_nb * 4 * NTW;
+  auto load_w = [&](WStage& st, int f) {
+    int nb, c;
+    pos(f, nb, c);
+    const int t0 = nb * 4 * NTW;
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, voff_w, (t0 + nt) * tile_bytes + l_c * kWBlockBytes, kNonTemporal);
+      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, voff_w, (t0 + nt) * tile_bytes + c * kWBlockBytes, kNonTemporal);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
-                                                     ((t0 + nt) * KC + l_c) * kSBlockBytes, 0);
-    if constexpr (XL) {
+      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
+                                                      ((t0 + nt) * KC + c) * kSBlockBytes, 0);
+  };
+  auto load_x = [&](auto buf_id, int f) {
+    constexpr int b = decltype(buf_id)::value;
+    int nb, c;
+    pos(f, nb, c);
 #pragma unroll
-      for (int i = 0; i < NXL; ++i) {
-        const int vo = (int)voff_x[i];
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(s_x + (w * D + d) * XBUF + 4 * i * XROW),
-            16, vo, l_c * XROW, 0, 0);
-      }
-    } else {
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          s.x[tm][g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x[tm] + g * 64, l_c * XROW, 0);
-    }
-    if (++l_c == KC) {
-      l_c = 0;
-      ++l_nb;
+    for (int i = 0; i < NX; ++i) {
+      const int vo = (int)voff_x[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra,
+          (__attribute__((address_space(3))) void*)(s_x + b * XBUF + 4 * (w * NX + i) * XROW),
+          16, vo, c * XROW, 0, 0);
     }
   };
 
@@ -731,57 +878,41 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
     for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
   const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
-  // LDS operand reads: lane l takes row tm*16 + l%16, segment 4g + l/16,
-  // stored at slot segment ^ (l % 16); tiles differ by 16 rows (offset).
-  const uint32_t xrd = lds_addr(s_x) + (uint32_t)(w * D) * XBUF + col * XROW;
+  // operand read: row tm*16 + l%16, segment 4g + l/16 at slot segment ^ (l%16)
+  const uint32_t xrd = lds_addr(s_x) + col * XROW;
 
-  // compute cursor: column block and chunk of the next stage to consume
   int c_nb = nb0, c_c = 0;
-  auto step = [&](const Stage& s, auto d_id, auto tail) {
-    constexpr int d = decltype(d_id)::value;
-    if constexpr (XL) {
-      // this stage's token rows: in the steady loop D - 1 later stages'
-      // loads were issued after them; in the tail the count varies
-      if constexpr (decltype(tail)::value)
-        wait_vmcnt<0>();
-      else
-        wait_vmcnt<(D - 1) * (2 * NTW + NXL)>();
-    }
+  auto compute = [&](auto buf_id, const WStage& st) {
+    constexpr int b = decltype(buf_id)::value;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      const uint32_t a = xrd + b * XBUF + (((4 * g + kb) ^ col) << 4);
       u32x4 xg[TM];
-      if constexpr (XL) {
-        const uint32_t a = xrd + d * XBUF + (((4 * g + kb) ^ col) << 4);
-        xg[0] = lds_read16<0>(a);
-        if constexpr (TM > 1) xg[1] = lds_read16<16 * XROW>(a);
-        if constexpr (TM > 1) {
-          wait_lgkm<1>(xg[0]);
-          wait_lgkm<0>(xg[1]);
-        } else {
-          wait_lgkm<0>(xg[0]);
-        }
+      xg[0] = lds_read16<0>(a);
+      if constexpr (TM > 1) xg[1] = lds_read16<16 * XROW>(a);
+      if constexpr (TM > 1) {
+        wait_lgkm<1>(xg[0]);
+        wait_lgkm<0>(xg[1]);
       } else {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) xg[tm] = s.x[tm][g];
+        wait_lgkm<0>(xg[0]);
       }
-      f32x4 xs[TM];
+      f32x4 xsum[TM];
 #pragma unroll
-      for (int tm = 0; tm < TM; ++tm) xs[tm] = mfma16(xg[tm], neg136, zero4);
+      for (int tm = 0; tm < TM; ++tm) xsum[tm] = mfma16(xg[tm], neg136, zero4);
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
-        const u32x4 wb = unpack_128q(s.w[nt][g]);
-        const uint32_t sw = s.s[nt][g >> 1];
+        const u32x4 wb = unpack_128q(st.w[nt][g]);
+        const uint32_t sw = st.s[nt][g >> 1];
         const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
 #pragma unroll
         for (int tm = 0; tm < TM; ++tm) {
-          const f32x4 pr = mfma16(xg[tm], wb, xs[tm]);
+          const f32x4 pr = mfma16(xg[tm], wb, xsum[tm]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[nt][tm][r] = __builtin_fmaf(scv, pr[r], acc[nt][tm][r]);
         }
       }
     }
     if (++c_c == KC) {
-      // column block c_nb complete: lane holds rows tm*16 + 4*kb + r, column col
 #pragma unroll
       for (int nt = 0; nt < NTW; ++nt) {
         const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
@@ -799,38 +930,40 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
       ++c_nb;
     }
   };
-  using Loop = std::false_type;
-  using Tail = std::true_type;
 
-  // Same pipeline as the kernel above, over the flattened stream.
-  int f = 0;
-  if (total >= 2 * D) {
-    static_for<D>([&](auto d) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_next(st[d], d);
-    });
-    for (; f + 2 * D <= total; f += D) {
-      static_for<D>([&](auto d) {
-        __builtin_amdgcn_sched_barrier(0);
-        step(st[d], d, Loop{});
-        __builtin_amdgcn_sched_barrier(0);
-        load_next(st[d], d);
-      });
-    }
+  // Pipeline. Issue order: prologue W(0) X(0) W(1) X(1) .. X(D-2) W(D-1);
+  // step j: [wait, barrier] X(j+D-1) into the buffer of chunk j-1, compute
+  // chunk j, W(j+D). When step j waits, the loads issued after X(j) are
+  // W(j+1) and D-2 pairs (X, W): that count is exact on every step.
+  constexpr int kAfter = NW + (D - 2) * (NX + NW);
+  WStage ws[D];
+  static_for<D - 1>([&](auto d) {
+    load_w(ws[d], d);
+    load_x(d, d);
     __builtin_amdgcn_sched_barrier(0);
-  } else {
+  });
+  load_w(ws[D - 1], D - 1);
+  auto step = [&](int j, auto cur) {
+    constexpr int b = decltype(cur)::value;
+    wait_vmcnt<kAfter>();
+    lds_barrier();
+    load_x(std::integral_constant<int, (b + D - 1) % D>{}, j + D - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(cur, ws[b]);
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[b], j + D);
+  };
+  for (int j = 0;; j += D) {
+    bool done = false;
     static_for<D>([&](auto d) {
-      if (d < total) load_next(st[d], d);
-    });
-  }
-  for (; f < total; f += D) {
-    static_for<D>([&](auto d) {
-      if (f + d < total) {
-        step(st[d], d, Tail{});
-        if (f + d + D < total) load_next(st[d], d);
+      if (!done) {
+        step(j + d, d);
+        if (j + d + 1 >= total) done = true;
       }
     });
+    if (done) break;
   }
+  wait_vmcnt<0>();
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
@@ -929,16 +1062,6 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
                cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
 }
 
-// Bare workgroup barrier. __syncthreads() also fences memory, and that
-// fence waits for every outstanding direct-to-LDS load, including prefetches
-// of later chunks. The waits this kernel needs are explicit vmcnt counts,
-// and the asm clobbers keep the compiler from moving memory operations
-// across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p) {
   constexpr int BM = kLmBM;
@@ -1278,25 +1401,26 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
   const int depth = pl.k_depth / kChunkK;
-  const bool xl = tm == 2 && wk == 1 && gp.split == 1 && (ntw == 2 || ntw == 4);
-  if (pl.n_stream > 1 || xl) {
-    // one K partition: the streaming kernel (16-row tiles streaming column
-    // blocks, or 32-row tiles with token rows staged in LDS)
+  const bool xs = tm == 2 && wk == 1 && gp.split == 1 && pl.n_stream == 1 &&
+                  (ntw == 2 || ntw == 4);
+  if (pl.n_stream > 1 || xs) {
+    // one K partition: 16-row tiles streaming column blocks, or 32-row tiles
+    // with the token rows shared through LDS
     if (wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) || ntw * 64 != pl.block_n ||
-        (tm != 1 && tm != 2))
+        (pl.n_stream > 1 && tm != 1))
       return (int)hipErrorInvalidConfiguration;
     gp.nstream = pl.n_stream;
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
     const dim3 sg((unsigned)(tiles_pad * gp.nblocks));
-    if (tm == 1 && ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<1, 4, 4, false>), sg, dim3(256), 0, st, gp);
-    else if (tm == 1)
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<1, 2, 4, false>), sg, dim3(256), 0, st, gp);
+    if (xs && ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 4, 2>), sg, dim3(256), 0, st, gp);
+    else if (xs)
+      hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);
     else if (ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4, 2, true>), sg, dim3(256), 0, st, gp);
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), sg, dim3(256), 0, st, gp);
     else
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 2, 2, true>), sg, dim3(256), 0, st, gp);
+      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), sg, dim3(256), 0, st, gp);
     return (int)hipGetLastError();
   }
   if (!small_m_supported(tm, ntw) || (wk != 1 && wk != 2 && wk != 4) ||
