@@ -77,22 +77,38 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->kernel = QMA_KERNEL_SMALL_M;
   p->block_m = bm;
   const int tm = bm / 16;
-  // The four waves of a workgroup split K in two when K is long (each wave
-  // still streams >= 12 chunks of 128) and split the columns otherwise.
-  // 32-row tiles keep one K partition: their kernel stages token rows in
-  // per-wave LDS buffers, which fits the register budget only that way.
-  int wk = (tm == 1 && L.k_chunks >= 24) ? 2 : 1;
-  if (L.N % (16 * (4 / wk)) != 0) wk = 4;
+  int wk, ntw = 0;
+  if (tm <= 2) {
+    // 16- and 32-row tiles: one K partition, the four waves side by side,
+    // token rows shared through LDS (16 * 4 * ntw columns per workgroup).
+    // 16-row tiles take 128 columns, except with short K where the
+    // workgroup streams column blocks (below) and the wider block is better.
+    wk = 1;
+    ntw = (tm == 2 || L.k_chunks < qma::kStreamChunks) ? 4 : 2;
+    while (ntw > 1 && L.N % (64 * ntw) != 0) ntw /= 2;
+    // Wave-aware width: the narrower width when the wide one leaves CUs
+    // without a workgroup; an underfilled grid is then left to split-K.
+    if (ntw > 1 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
+        L.N % (64 * (ntw / 2)) == 0)
+      ntw /= 2;
+  } else {
+    // 64-row tiles: the four waves split K in two when K is long (each wave
+    // still streams >= 12 chunks of 128) and split the columns otherwise.
+    wk = L.k_chunks >= 24 ? 2 : 1;
+    if (L.N % (16 * (4 / wk)) != 0) wk = 4;
+    const int wn0 = 4 / wk;
+    for (int cand : {4, 2, 1})
+      if (!ntw && qma::small_m_supported(tm, cand) && L.N % (16 * wn0 * cand) == 0) ntw = cand;
+    if (ntw == 4 && (int64_t)tiles_m * (L.N / (16 * wn0 * 4)) < qma::kNumCUs &&
+        L.N % (16 * wn0 * 2) == 0)
+      ntw = 2;
+  }
+  if (L.N % (16 * (4 / wk) * ntw) != 0) {
+    // odd widths (N a multiple of 16 only): one tile per wave, waves on K
+    wk = 4;
+    ntw = 1;
+  }
   const int wn = 4 / wk;
-  int ntw = 0;
-  for (int cand : {4, 2, 1})
-    if (!ntw && qma::small_m_supported(tm, cand) && L.N % (16 * wn * cand) == 0) ntw = cand;
-  // Wave-aware width: the narrower of the two widths when the wide one
-  // leaves CUs without a workgroup; an underfilled grid is then left to
-  // split-K.
-  if (ntw == 4 && (int64_t)tiles_m * (L.N / (16 * wn * 4)) < qma::kNumCUs &&
-      L.N % (16 * wn * 2) == 0)
-    ntw = 2;
   p->waves_k = wk;
   p->block_n = 16 * wn * ntw;
   const int32_t tiles =
@@ -107,7 +123,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     split = std::max<int32_t>(split, 1);
   }
   p->split_k = split;
-  p->k_depth = (tm == 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw)) *
+  // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
+  // chunks in flight per wave at three workgroups per CU
+  p->k_depth = (tm <= 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw)) *
                qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
   // only one or two chunks would spend its life on start-up and one memory

@@ -781,8 +781,8 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 // loads of chunk j (wait count) and, past the barrier, every wave is done
 // with chunk j-1, whose buffer then takes chunk j+D-1. Sharing the rows
 // keeps the LDS (D * TM * 4 KiB) and register budget small enough for three
-// workgroups per CU, which the 32-token tiles of a masked decode need to keep
-// HBM busy, and loads each row once per workgroup instead of once per wave.
+// workgroups per CU, which decode grids need to keep HBM busy, and loads
+// each row once per workgroup instead of once per wave.
 template <int TM, int NTW, int D>
 __global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParams p) {
   constexpr int XROW = 256;
@@ -1401,11 +1401,11 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
   const int depth = pl.k_depth / kChunkK;
-  const bool xs = tm == 2 && wk == 1 && gp.split == 1 && pl.n_stream == 1 &&
+  const bool xs = (tm == 1 || tm == 2) && wk == 1 && gp.split == 1 && pl.n_stream == 1 &&
                   (ntw == 2 || ntw == 4);
   if (pl.n_stream > 1 || xs) {
-    // one K partition: 16-row tiles streaming column blocks, or 32-row tiles
-    // with the token rows shared through LDS
+    // one K partition: 16-row tiles streaming column blocks, or 16/32-row
+    // tiles with the token rows shared through LDS
     if (wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) || ntw * 64 != pl.block_n ||
         (pl.n_stream > 1 && tm != 1))
       return (int)hipErrorInvalidConfiguration;
@@ -1413,7 +1413,11 @@ int launch_gemm(const GemmArgs& g, void* stream) {
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
     const dim3 sg((unsigned)(tiles_pad * gp.nblocks));
-    if (xs && ntw == 4)
+    if (xs && tm == 1 && ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 4, 2>), sg, dim3(256), 0, st, gp);
+    else if (xs && tm == 1)
+      hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 2, 2>), sg, dim3(256), 0, st, gp);
+    else if (xs && ntw == 4)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 4, 2>), sg, dim3(256), 0, st, gp);
     else if (xs)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);

@@ -88,7 +88,8 @@ def _plan(E, N, K, T, topk, force=0):
 def test_plan_decode_ep8():
     p = _plan(48, 4096, 7168, 576, 1)
     assert p.kernel == qma.KERNEL_SMALL_M and p.block_m == 16
-    assert p.block_n == 128 and p.waves_k == 2 and p.split_k == 1  # 48 x 32 tiles
+    assert p.block_n == 128 and p.waves_k == 1 and p.split_k == 1  # 48 x 32 tiles
+    assert p.k_depth == 256                            # shared-row kernel: 2 chunks
     assert p.tok_e_x100 == 1200 and p.rows == 576
     assert qma.qma_workspace_bytes(p) == 0
 
@@ -96,12 +97,17 @@ def test_plan_decode_ep8():
 def test_plan_tp8_and_tiny():
     p = _plan(384, 512, 7168, 256, 8)
     assert p.block_m == 16 and p.tok_e_x100 == 533 and p.split_k == 1
+    assert p.waves_k == 1 and p.block_n == 128         # 383 x 4 tiles
     t = _plan(8, 256, 256, 64, 2)
-    assert t.block_m == 16 and t.waves_k == 1          # K = 256: waves split columns
-    assert t.block_n == 128                            # 16 tiles: the narrower width
+    assert t.block_m == 16 and t.waves_k == 1          # waves side by side on columns
+    assert t.block_n == 128                            # short K: 256 wide, 8 tiles -> narrower
     assert t.split_k == 1                              # K = 256: no room to split
     d = _plan(48, 7168, 2048, 576, 1)                  # EP8 down: K = 2048
-    assert d.waves_k == 1 and d.block_n == 256 and d.split_k == 1
+    assert d.waves_k == 1 and d.block_n == 128 and d.split_k == 1
+    m = _plan(48, 4096, 7168, 48 * 32, 1)              # 32-row tiles: 256 columns
+    assert m.block_m == 32 and m.waves_k == 1 and m.block_n == 256
+    big = _plan(48, 4096, 7168, 48 * 64, 1)            # 64-row tiles: K split in two
+    assert big.block_m == 64 and big.waves_k == 2
 
 
 def test_block_m_follows_tok_e():
