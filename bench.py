@@ -160,6 +160,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle CPU work for cpu_baseline (0 = skip)")
+    ap.add_argument("--schedule", default="semi_static", choices=("semi_static", "dynamic"),
+                    help="how small-M GEMMs hand out (tile, column block) work; dynamic "
+                         "applies where the plan accepts it (16/32-row tiles, one K "
+                         "partition)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a buffer of this many bytes 3 times (a "
                          "plain copy kernel of known size, to calibrate rocprofv3 "
@@ -204,6 +208,9 @@ def main():
         a = to_device(wl["a"])
         stages = [("gate_up", lambda: moe.gate_up(a, index)), ("silu_and_mul", moe.act),
                   ("down", lambda: moe.down(index))]
+    sched_applied = (False, False)
+    if args.schedule == "dynamic":
+        sched_applied = moe.set_schedule(qma.SCHEDULE_DYNAMIC)
     stream = torch.cuda.current_stream()
 
     for _ in range(args.warmup):
@@ -269,7 +276,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload,
                    "rows": work["rows"], "weights": "uint4 group-32 bf16 scales, zero point 8",
-                   "parallelism": "one EP/TP rank's share on one GPU"},
+                   "parallelism": "one EP/TP rank's share on one GPU",
+                   "schedule": {"gate_up": "dynamic" if sched_applied[0] else "semi_static",
+                                "down": "dynamic" if sched_applied[1] else "semi_static"}},
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
         "kernel_us_mean": {k: round(v, 2) for k, v in us.items()},
         "kernel_us_median": {k: round(v, 2) for k, v in med.items()},

@@ -118,7 +118,26 @@ typedef struct qma_plan {
   int32_t waves_k;       /* K partitions inside one workgroup */
   int32_t expected_m;    /* masked layers: the expected_m planned for, else 0 */
   int32_t n_stream;      /* N blocks one workgroup streams through (>= 1) */
+  int32_t schedule;      /* QMA_SCHEDULE_*: how (tile, column block) work is handed out */
 } qma_plan_t;
+
+/* How a small-M GEMM hands out its (token tile, column block) work
+ * ([announce] scheduling section: semi-static token-slice scheduling
+ * against dynamic scheduling at 9..15 tokens per expert).
+ *   SEMI_STATIC: the grid is sized from host-known shapes and each
+ *     workgroup derives its tile, expert and rows from the routing buffers
+ *     on the device; workgroups past num_tokens_padded exit at once. The
+ *     planner's default.
+ *   DYNAMIC: a persistent grid (three workgroups per CU) whose workgroups
+ *     take items from a device work counter until the routed items run
+ *     out. The counter lives in the workspace (qma_workspace_bytes counts
+ *     it) and is reset by a one-thread kernel on the same stream before the
+ *     GEMM. Only 16/32-row tiles with one K partition, no split-K and
+ *     n_stream = 1 accept it; other plans -> QMA_ERR_INVALID_ARG. */
+typedef enum {
+  QMA_SCHEDULE_SEMI_STATIC = 0,
+  QMA_SCHEDULE_DYNAMIC = 1
+} qma_schedule;
 
 /* ---- layer (load time) ------------------------------------------------ */
 
@@ -182,7 +201,9 @@ qma_status qma_plan_indexed(const qma_layer_t* layer, int32_t T, int32_t topk,
 qma_status qma_plan_grouped(const qma_layer_t* layer, int32_t m_rows_or_budget,
                             int32_t expected_m, qma_plan_t* out);
 
-/* Bytes of fp32 split-K workspace the plan's GEMM needs (0 if split is off). */
+/* Bytes of workspace the plan's GEMM needs: the fp32 split-K partials when
+ * split is on, plus 256 bytes for the work counter of a DYNAMIC schedule
+ * (0 for a semi-static plan without split). */
 size_t qma_workspace_bytes(const qma_plan_t* plan);
 
 /* ---- routing ---------------------------------------------------------- */

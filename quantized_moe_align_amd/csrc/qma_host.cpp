@@ -199,6 +199,12 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
   if (plan->split_k < 1 || plan->split_k > 8)
     return fail(QMA_ERR_INVALID_ARG, "plan has bad split_k %d", plan->split_k);
+  if (plan->schedule != QMA_SCHEDULE_SEMI_STATIC &&
+      (plan->schedule != QMA_SCHEDULE_DYNAMIC || plan->kernel != QMA_KERNEL_SMALL_M ||
+       plan->waves_k != 1 || plan->split_k != 1 || plan->n_stream != 1 ||
+       (plan->block_m != 16 && plan->block_m != 32) ||
+       (plan->block_n != 128 && plan->block_n != 256)))
+    return fail(QMA_ERR_INVALID_ARG, "plan has bad schedule %d", plan->schedule);
   if (plan->n_stream < 1 || plan->n_stream > 64 ||
       (plan->n_stream > 1 && (plan->kernel != QMA_KERNEL_SMALL_M || plan->waves_k != 1 ||
                               plan->split_k != 1 || plan->block_m != 16)))
@@ -213,8 +219,10 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
 }
 
 size_t ws_bytes_for(const qma_plan_t* p, int64_t rows) {
-  if (p->split_k <= 1) return 0;
-  return (size_t)p->split_k * (size_t)rows * (size_t)p->n * sizeof(float);
+  size_t b = 0;
+  if (p->split_k > 1) b = (size_t)p->split_k * (size_t)rows * (size_t)p->n * sizeof(float);
+  if (p->schedule == QMA_SCHEDULE_DYNAMIC) b = (b + 255) / 256 * 256 + qma::kWorkCounterBytes;
+  return b;
 }
 
 qma_status check_ws(const qma_plan_t* plan, int64_t rows, const void* ws,

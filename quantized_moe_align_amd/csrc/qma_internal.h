@@ -26,6 +26,8 @@ constexpr int kMaxExperts = 1024;  // moe_align's single-workgroup limit
 constexpr int kNumCUs = 256;
 // chunks a streaming small-M workgroup aims to keep in its load pipeline
 constexpr int kStreamChunks = 8;
+// bytes at the end of the workspace holding a dynamic schedule's counter
+constexpr int kWorkCounterBytes = 256;
 
 struct Layer {
   int32_t E, N, K;

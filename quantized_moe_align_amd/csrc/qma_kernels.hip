@@ -272,6 +272,7 @@ struct GemmParams {
   int32_t Mb, tiles_per_expert, rows_cap, cap;
   int32_t E, N, K, NT, KC, BM;
   int32_t nstream, nbtot;  // streaming small-M: N blocks per workgroup, N blocks in all
+  int32_t* work;            // dynamic schedule: work counter (workspace)
 };
 
 struct RowInfo {
@@ -783,17 +784,18 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 // keeps the LDS (D * TM * 4 KiB) and register budget small enough for three
 // workgroups per CU, which decode grids need to keep HBM busy, and loads
 // each row once per workgroup instead of once per wave.
+template <int TM, int D>
+constexpr int xs_lds_bytes() { return D * TM * 16 * 256; }
+
+// One (token tile, column group) of the shared-row kernel; s_x holds
+// xs_lds_bytes<TM, D>() bytes of LDS.
 template <int TM, int NTW, int D>
-__global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParams p) {
+__device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, uint8_t* s_x) {
   constexpr int XROW = 256;
   constexpr int XBUF = TM * 16 * XROW;       // one chunk of the tile's token rows
   constexpr int NX = TM;                     // direct-to-LDS loads per wave and chunk
   constexpr int NW = 2 * NTW;                // weight + scale loads per wave and chunk
   static_assert(D >= 2, "pipeline depth");
-  __shared__ __attribute__((aligned(1024))) uint8_t s_x[D * XBUF];
-
-  int tile, grp, sp;
-  if (!decode_bid(p, tile, grp, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
   if (e < 0) return;
 
@@ -964,6 +966,41 @@ __global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParam
     if (done) break;
   }
   wait_vmcnt<0>();
+}
+
+// Semi-static schedule: the grid covers every (tile, column group) the
+// host can bound; a workgroup derives its item from its index and the
+// routing buffers, and items past the routed ones exit at once.
+template <int TM, int NTW, int D>
+__global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[xs_lds_bytes<TM, D>()];
+  int tile, grp, sp;
+  if (!decode_bid(p, tile, grp, sp)) return;
+  xs_tile<TM, NTW, D>(p, tile, grp, s_x);
+}
+
+// Dynamic schedule: a persistent grid whose workgroups take (tile, column
+// group) items from the work counter until the routed items run out.
+template <int TM, int NTW, int D>
+__global__ __launch_bounds__(256, 3) void gemm_small_m_xs_dyn_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[xs_lds_bytes<TM, D>()];
+  __shared__ int s_item;
+  const int ntiles = p.mode == 0 ? min(*p.ntp / p.BM, p.num_tiles) : p.num_tiles;
+  const int items = ntiles * p.nblocks;
+  for (;;) {
+    if (threadIdx.x == 0) s_item = atomicAdd(p.work, 1);
+    __syncthreads();
+    const int it = __builtin_amdgcn_readfirstlane(s_item);
+    if (it >= items) break;
+    const int tile = it / p.nblocks;
+    xs_tile<TM, NTW, D>(p, tile, it - tile * p.nblocks, s_x);
+    // every wave is done with s_item and the LDS ring before the next item
+    __syncthreads();
+  }
+}
+
+__global__ void reset_counter_kernel(int32_t* c) {
+  if (threadIdx.x == 0) *c = 0;
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
@@ -1403,6 +1440,23 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int depth = pl.k_depth / kChunkK;
   const bool xs = (tm == 1 || tm == 2) && wk == 1 && gp.split == 1 && pl.n_stream == 1 &&
                   (ntw == 2 || ntw == 4);
+  if (pl.schedule == QMA_SCHEDULE_DYNAMIC) {
+    if (!xs || g.ws == nullptr) return (int)hipErrorInvalidConfiguration;
+    gp.nstream = 1;
+    gp.nbtot = gp.nblocks;
+    gp.work = (int32_t*)g.ws;
+    hipLaunchKernelGGL(reset_counter_kernel, dim3(1), dim3(64), 0, st, gp.work);
+    const dim3 dg((unsigned)(3 * kNumCUs));
+    if (tm == 1 && ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_xs_dyn_kernel<1, 4, 2>), dg, dim3(256), 0, st, gp);
+    else if (tm == 1)
+      hipLaunchKernelGGL((gemm_small_m_xs_dyn_kernel<1, 2, 2>), dg, dim3(256), 0, st, gp);
+    else if (ntw == 4)
+      hipLaunchKernelGGL((gemm_small_m_xs_dyn_kernel<2, 4, 2>), dg, dim3(256), 0, st, gp);
+    else
+      hipLaunchKernelGGL((gemm_small_m_xs_dyn_kernel<2, 2, 2>), dg, dim3(256), 0, st, gp);
+    return (int)hipGetLastError();
+  }
   if (pl.n_stream > 1 || xs) {
     // one K partition: 16-row tiles streaming column blocks, or 16/32-row
     // tiles with the token rows shared through LDS

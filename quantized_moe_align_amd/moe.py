@@ -68,6 +68,13 @@ def workspace_for(plan: qma.Plan, device="cuda") -> Optional[torch.Tensor]:
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
+def schedule_applies(plan: qma.Plan) -> bool:
+    """Whether a plan can take the dynamic schedule (16/32-row small-M tiles
+    with one K partition, no split-K, no column-block streaming)."""
+    return (plan.kernel == qma.KERNEL_SMALL_M and plan.waves_k == 1 and plan.split_k == 1
+            and plan.n_stream == 1 and plan.block_m in (16, 32) and plan.block_n in (128, 256))
+
+
 @dataclass
 class Routing:
     sorted_ids: torch.Tensor
@@ -104,11 +111,25 @@ class IndexedMoE:
         self.c2 = empty_bf16(max(R, 1), self.K, device=dev)
         self.ws13 = workspace_for(self.plan13, dev)
         self.ws2 = workspace_for(self.plan2, dev)
+        self._dev = dev
 
     def align(self, topk_ids: torch.Tensor, stream=None):
         r = self.routing
         qma.qma_moe_align(topk_ids, self.T, self.topk, self.E, r.block_m, r.sorted_ids,
                           r.expert_ids, r.ntp, r.cap, stream)
+
+    def set_schedule(self, schedule: int) -> tuple:
+        """Switch both GEMMs to `schedule` where their plan accepts it;
+        returns which of (gate_up, down) changed."""
+        done = []
+        for name in ("13", "2"):
+            plan = getattr(self, "plan" + name)
+            ok = schedule == qma.SCHEDULE_SEMI_STATIC or schedule_applies(plan)
+            if ok:
+                plan.schedule = schedule
+                setattr(self, "ws" + name, workspace_for(plan, self._dev))
+            done.append(ok)
+        return tuple(done)
 
     def gate_up(self, a: torch.Tensor, stream=None):
         r = self.routing
@@ -156,6 +177,7 @@ class GroupedMoE:
         self.c2 = empty_bf16(max(rows, 1), self.K, device=device)
         self.ws13 = workspace_for(self.plan13, device)
         self.ws2 = workspace_for(self.plan2, device)
+        self._dev = device
 
     def _gemm(self, w, plan, a, c, ws, index, stream):
         wsb = 0 if ws is None else ws.numel()
@@ -165,6 +187,19 @@ class GroupedMoE:
         else:
             qma.qma_grouped_contiguous_gemm(w.layer, plan, a, index, self.rows, w.packed, c,
                                             ws, wsb, stream)
+
+    def set_schedule(self, schedule: int) -> tuple:
+        """Switch both GEMMs to `schedule` where their plan accepts it;
+        returns which of (gate_up, down) changed."""
+        done = []
+        for name in ("13", "2"):
+            plan = getattr(self, "plan" + name)
+            ok = schedule == qma.SCHEDULE_SEMI_STATIC or schedule_applies(plan)
+            if ok:
+                plan.schedule = schedule
+                setattr(self, "ws" + name, workspace_for(plan, self._dev))
+            done.append(ok)
+        return tuple(done)
 
     def gate_up(self, a, index, stream=None):
         self._gemm(self.w13, self.plan13, a, self.c1, self.ws13, index, stream)

@@ -15,6 +15,8 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqma.so")
 
+SCHEDULE_SEMI_STATIC, SCHEDULE_DYNAMIC = 0, 1
+
 QMA_OK, QMA_ERR_INVALID_ARG, QMA_ERR_UNSUPPORTED, QMA_ERR_ROUTING, \
     QMA_ERR_WORKSPACE, QMA_ERR_HIP = range(6)
 PATH_INDEXED, PATH_GROUPED_CONTIGUOUS, PATH_GROUPED_MASKED = 0, 1, 2
@@ -59,7 +61,7 @@ class Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "path", "kernel", "block_m", "block_n", "split_k", "k_depth",
         "num_experts", "n", "k", "rows", "tok_e_x100", "est_tiles", "profile",
-        "waves_k", "expected_m", "n_stream")]
+        "waves_k", "expected_m", "n_stream", "schedule")]
 
     def as_dict(self):
         return {n: getattr(self, n) for n, _ in self._fields_}

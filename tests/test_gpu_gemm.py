@@ -462,3 +462,52 @@ def test_stream_random_topk_weights_and_grouped(gpu):
     assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N), row_e.reshape(-1),
                       "stream masked")
     assert np.all(got_m[row_e < 0] == SENT)
+
+
+# Dynamic schedule (a persistent grid taking (tile, column block) items from
+# a work counter) against the semi-static grid: same kernel body, so the
+# outputs must agree bit for bit, and with integer-exact inputs both equal
+# the oracle.
+@pytest.mark.parametrize("bm,bn", [(16, 128), (16, 256), (32, 256), (32, 128)])
+def test_dynamic_schedule_matches_semi_static(gpu, bm, bn):
+    E, T, topk, K, N = 7, 90, 2, 512, 768 if bn == 256 else 640
+    if N % bn:
+        N = bn * 3
+    rng = np.random.default_rng(100 + bm + bn)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": bm, "block_n": bn, "waves_k": 1,
+          "split_k": 1, "n_stream": 1}
+    static, _ = indexed(a, topk, ids, w, s, force_bm=bm, override=ov)
+    dyn, plan = indexed(a, topk, ids, w, s, force_bm=bm,
+                        override=dict(ov, schedule=qma.SCHEDULE_DYNAMIC))
+    assert plan.schedule == qma.SCHEDULE_DYNAMIC
+    assert np.array_equal(dyn, static)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(dyn[valid], rne(ref[valid]))
+    assert np.all(dyn[~valid] == SENT)
+
+
+def test_dynamic_schedule_grouped(gpu):
+    E, K, N = 5, 512, 512
+    rng = np.random.default_rng(110)
+    w, s = weights(rng, E, N, K)
+    wl = inputs.make_contiguous("c", 6, E, 0, K, N // 2, counts=[20, 0, 7, 16, 33],
+                                weights=False)
+    m_idx = wl["m_indices"]
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": 16, "block_n": 128, "waves_k": 1,
+          "split_k": 1, "n_stream": 1}
+    got = contiguous(wl["a"], m_idx, w, s, dict(ov, schedule=qma.SCHEDULE_DYNAMIC))
+    assert np.array_equal(got, contiguous(wl["a"], m_idx, w, s, ov))
+    Mb = 64
+    masked_m = np.array([32, 0, 64, 1, 17], np.int32)
+    am = inputs.bf16_normal(rng, (E, Mb, K))
+    ovm = dict(ov, block_m=32, block_n=256)
+    got_m = masked(am, masked_m, 32, w, s, dict(ovm, schedule=qma.SCHEDULE_DYNAMIC))
+    assert np.array_equal(got_m, masked(am, masked_m, 32, w, s, ovm))
+    ref_m = O.grouped_masked(am, masked_m, w, s)
+    row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
+    assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N), row_e.reshape(-1),
+                      "dynamic masked")

@@ -138,6 +138,16 @@ def test_stream_rule():
     assert _plan(8, 256, 128, 64, 2).n_stream == 1          # grid too small to stream
 
 
+def test_dynamic_schedule_plan_rules():
+    p = _plan(48, 4096, 7168, 576, 1)
+    assert p.schedule == qma.SCHEDULE_SEMI_STATIC and qma.qma_workspace_bytes(p) == 0
+    p.schedule = qma.SCHEDULE_DYNAMIC
+    assert qma.qma_workspace_bytes(p) == 256           # the work counter
+    q = _plan(1, 4096, 7168, 12, 1)                    # split-K plan
+    q.schedule = qma.SCHEDULE_DYNAMIC
+    assert qma.qma_workspace_bytes(q) == q.split_k * 12 * 4096 * 4 + 256
+
+
 def test_large_m_rule():
     # indexed: large-M from 80 routed rows per expert, or on request
     assert _plan(48, 4096, 7168, 48 * 80, 1).kernel == qma.KERNEL_LARGE_M
