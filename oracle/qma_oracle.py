@@ -289,3 +289,30 @@ def moe_combine(c2: np.ndarray, topk_weights: np.ndarray, topk: int):
     T = c2.shape[0] // topk
     w = np.asarray(topk_weights, dtype=np.float64).reshape(T, topk)
     return (c2.reshape(T, topk, -1) * w[:, :, None]).sum(axis=1)
+
+
+def router_topk(logits, topk: int):
+    """Router of the MoE layer, the step before moe_align (the pages' decode
+    and prefill scenarios route each token to its top-k experts). Reading
+    adopted: weights are the softmax over all E experts, not renormalised
+    over the chosen k; the k experts are those with the largest logits
+    (softmax is monotone, so this is the largest-probability choice without
+    rounding ties), equal logits going to the lower expert index.
+
+    logits: [T, E] float32. Returns (topk_ids [T, topk] int32,
+    topk_weights [T, topk] float64), ids in descending order of logit."""
+    lg = np.asarray(logits, dtype=np.float64)
+    T, E = lg.shape
+    ids = np.empty((T, topk), dtype=np.int32)
+    w = np.empty((T, topk), dtype=np.float64)
+    for t in range(T):
+        row = lg[t]
+        m = row.max()
+        ex = np.exp(row - m)
+        p = ex / ex.sum()
+        # descending logit, lower index first on equal logits
+        order = sorted(range(E), key=lambda e: (-row[e], e))[:topk]
+        ids[t] = order
+        w[t] = p[order]
+    return ids, w
+
