@@ -314,6 +314,25 @@ qma_status qma_grouped_masked_gemm(const qma_layer_t* layer,
                                    uint16_t* c, void* ws, size_t ws_bytes,
                                    void* stream);
 
+/* ---- router --------------------------------------------------------- */
+
+/* The router step before moe_align: each token goes to its top-k experts
+ * (the pages' scenarios route tokens top-k over the layer's experts,
+ * [announce] measurement section; [release] performance highlights).
+ * For token t, topk_ids[t, 0..topk) are the experts with the largest
+ * logits, best first, equal logits going to the lower expert index, and
+ * topk_weights[t, i] is that expert's softmax probability over all E
+ * experts (not renormalised over the chosen k).
+ *   logits       [T, E] float32, finite values (others: unspecified result)
+ *   topk_ids     [T, topk] int32 out
+ *   topk_weights [T, topk] float32 out (may be NULL)
+ * All device buffers, 4-byte aligned. Errors: T < 0, E outside [1, 1024],
+ * topk outside [1, min(E, 16)], a null required buffer ->
+ * QMA_ERR_INVALID_ARG. */
+qma_status qma_router_topk(const float* logits, int32_t T, int32_t E,
+                           int32_t topk, int32_t* topk_ids,
+                           float* topk_weights, void* stream);
+
 /* ---- activation and combine ------------------------------------------- */
 
 /* The gated activation between gate_up and down ([announce] measurement

@@ -630,6 +630,18 @@ qma_status qma_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I
   return hip_status(qma::launch_silu_and_mul(x, y, R, I, stream), "silu_and_mul launch");
 }
 
+qma_status qma_router_topk(const float* logits, int32_t T, int32_t E, int32_t topk,
+                           int32_t* topk_ids, float* topk_weights, void* stream) {
+  if (T < 0 || E < 1 || E > 1024 || topk < 1 || topk > std::min(E, 16))
+    return fail(QMA_ERR_INVALID_ARG, "bad sizes T=%d E=%d topk=%d", T, E, topk);
+  if (T == 0) return ok();
+  if (!logits || !topk_ids) return fail(QMA_ERR_INVALID_ARG, "null buffer");
+  if (!aligned(logits, 4) || !aligned(topk_ids, 4) || (topk_weights && !aligned(topk_weights, 4)))
+    return fail(QMA_ERR_INVALID_ARG, "buffers must be 4-byte aligned");
+  return hip_status(qma::launch_router_topk(logits, T, E, topk, topk_ids, topk_weights, stream),
+                    "router launch");
+}
+
 qma_status qma_moe_combine(const uint16_t* c2, const float* w, const int32_t* topk_ids,
                            int32_t E, int32_t T, int32_t topk, int32_t N, uint16_t* out,
                            void* stream) {

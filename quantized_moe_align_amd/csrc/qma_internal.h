@@ -78,6 +78,8 @@ int launch_prepack(const Layer& L, const int32_t* qweight,
 int launch_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I,
                         void* stream);
 int launch_gemm(const GemmArgs& g, void* stream);
+int launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t topk,
+                       int32_t* ids, float* w, void* stream);
 int launch_combine(const uint16_t* c2, const float* w, const int32_t* ids,
                    int32_t E, int32_t T, int32_t topk, int32_t N,
                    uint16_t* out, void* stream);

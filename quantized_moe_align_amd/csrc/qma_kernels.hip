@@ -1571,6 +1571,78 @@ int launch_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I, vo
 // Top-k combine: out[t, n] = sum_k w[t, k] * c2[t*topk + k, n], fp32 sums in
 // k order, slots of experts outside [0, E) skipped when ids are given.
 // ---------------------------------------------------------------------------
+// ---------------------------------------------------------------------------
+// Router: softmax over the E logits of a token and its top-k experts, one
+// wave per token with the row in registers (E <= 1024: 16 per lane). The
+// choice compares logits (softmax is monotone, so no rounding can reorder
+// it), k rounds of a wave argmax over the experts not yet chosen, the
+// larger logit winning and the lower index on a tie.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ bool router_better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+__global__ __launch_bounds__(256) void router_topk_kernel(const float* __restrict__ logits,
+                                                          int T, int E, int topk,
+                                                          int32_t* __restrict__ ids,
+                                                          float* __restrict__ w) {
+  constexpr int PER = 16;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (size_t)t * E;
+  float v[PER];
+  float m = -__builtin_huge_valf();
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? row[e] : -__builtin_huge_valf();
+    m = fmaxf(m, v[i]);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i)
+    if (lane + 64 * i < E) sum += expf(v[i] - m);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o);
+  uint32_t taken = 0;  // bit i: expert lane + 64 i already chosen
+  for (int k = 0; k < topk; ++k) {
+    float bv = -__builtin_huge_valf();
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E && !((taken >> i) & 1u) && router_better(v[i], e, bv, bi)) {
+        bv = v[i];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (router_better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == (bi & 63)) taken |= 1u << (bi >> 6);
+    if (lane == 0) {
+      ids[(size_t)t * topk + k] = bi;
+      if (w) w[(size_t)t * topk + k] = expf(bv - m) / sum;
+    }
+  }
+}
+
+int launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t topk, int32_t* ids,
+                       float* w, void* stream) {
+  hipLaunchKernelGGL(router_topk_kernel, dim3((unsigned)((T + 3) / 4)), dim3(256), 0,
+                     (hipStream_t)stream, logits, T, E, topk, ids, w);
+  return (int)hipGetLastError();
+}
+
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t* __restrict__ c2,
                                                       const float* __restrict__ w,
                                                       const int32_t* __restrict__ ids,

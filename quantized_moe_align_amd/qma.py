@@ -32,7 +32,7 @@ EXPORTS = (
     "qma_plan_grouped", "qma_workspace_bytes", "qma_align_sizes",
     "qma_moe_align", "qma_validate_routing", "qma_validate_contiguous",
     "qma_indexed_gemm", "qma_grouped_contiguous_gemm",
-    "qma_grouped_masked_gemm", "qma_silu_and_mul", "qma_moe_combine",
+    "qma_grouped_masked_gemm", "qma_silu_and_mul", "qma_moe_combine", "qma_router_topk",
     "qma_status_str", "qma_last_error_detail", "qma_version",
 )
 
@@ -102,6 +102,7 @@ def lib():
                                               P, P, SZ, P]),
             "qma_silu_and_mul": (I32, [P, P, I64, I32, P]),
             "qma_moe_combine": (I32, [P, P, P, I32, I32, I32, I32, P, P]),
+            "qma_router_topk": (I32, [P, I32, I32, I32, P, P, P]),
             "qma_status_str": (ctypes.c_char_p, [I32]),
             "qma_last_error_detail": (ctypes.c_char_p, []),
             "qma_version": (ctypes.c_char_p, []),
@@ -236,6 +237,11 @@ def qma_grouped_masked_gemm(layer, plan: Plan, a, masked_m, Mb, expected_m, pack
 
 def qma_silu_and_mul(x, y, R, I, stream=None) -> None:
     _check(lib().qma_silu_and_mul(_ptr(x), _ptr(y), R, I, _stream(stream)))
+
+
+def qma_router_topk(logits, T, E, topk, topk_ids, topk_weights=None, stream=None) -> None:
+    _check(lib().qma_router_topk(_ptr(logits), T, E, topk, _ptr(topk_ids), _ptr(topk_weights),
+                                 _stream(stream)))
 
 
 def qma_moe_combine(c2, w, topk_ids, E, T, topk, N, out, stream=None) -> None:
