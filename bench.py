@@ -4,11 +4,13 @@
 One step is one pass of the whole hot path over one batch. On the indexed
 path that is moe_align, gate_up, silu_and_mul and down; on the grouped
 paths it is gate_up, silu_and_mul and down. Inputs are resident in HBM
-before timing starts. W warm-up steps run untimed, then exactly K steps
-run between device synchronisations. HIP events on the launching stream
-time each kernel. The per-layer gate_up+down time (the pages' kernel-level
-metric, which leaves out routing and activation) is reported next to the
-whole-step time.
+before timing starts. W warm-up steps run untimed (continued until the step
+has run back to back for --settle-ms, so that the clocks have left their
+idle ramp), then exactly K steps run back to back between device
+synchronisations: that wall time is ms_per_step. K further steps with HIP
+event pairs around every stage, on the launching stream, time each kernel.
+The per-layer gate_up+down time (the pages' kernel-level metric, which
+leaves out routing and activation) is reported next to the whole-step time.
 
 `value` is the whole step's effective throughput: algorithmic HBM bytes
 (decode shapes, GB/s) or algorithmic flops (prefill shapes, TFLOP/s)
@@ -33,7 +35,7 @@ sys.path.insert(0, ROOT)
 METRIC = ("gate_up+down µs/layer; effective HBM GB/s (decode) and TFLOP/s (prefill)")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-HBM_BOUND = {"ep8_decode", "tp8", "masked", "ep32_decode", "tiny"}
+HBM_BOUND = {"ep8_decode", "tp8", "masked", "ep16_decode", "ep32_decode", "tiny"}
 
 DESCRIPTIONS = {
     "ep8_decode": "indexed EP8 decode share: 48 experts x U{9..15} rows, hidden 7168, "
@@ -45,6 +47,7 @@ DESCRIPTIONS = {
     "contiguous": "grouped_contiguous: 48 experts x 128 rows, hidden 7168, intermediate 2048",
     "masked": "grouped_masked: 48 experts, budget 64, 32 valid rows, hidden 7168, "
               "intermediate 2048",
+    "ep16_decode": "indexed EP16 decode share: 24 experts x U{9..15} rows",
     "ep32_decode": "indexed EP32 decode share: 12 experts x U{9..15} rows",
     "tiny": "tiny: 8 experts, 64 tokens top-2, K 256, I 128",
 }
@@ -168,6 +171,13 @@ def main():
                     help="after the run, copy a buffer of this many bytes 3 times (a "
                          "plain copy kernel of known size, to calibrate rocprofv3 "
                          "FETCH_SIZE / WRITE_SIZE)")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="continue the untimed warm-up until the step has run back to "
+                         "back for this long (clock ramp from idle)")
+    ap.add_argument("--idle-gap-ms", type=float, default=0.0,
+                    help="idle the GPU this long before each timed step (untimed), to "
+                         "compare isolated launches with the sustained back-to-back "
+                         "default; ms_per_step is then the sum of the stage medians")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(json.dumps({"error": "this benchmark runs on exactly one GPU: the expert GEMM "
@@ -213,34 +223,55 @@ def main():
         sched_applied = moe.set_schedule(qma.SCHEDULE_DYNAMIC)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        for _, fn in stages:
-            fn()
+    # Warm-up: W steps, continued (untimed) until the GPU has run the step
+    # back-to-back for at least --settle-ms. From idle, the clocks take some
+    # tens of ms to reach their sustained level; steps timed inside that
+    # ramp measure the power state, not the kernels.
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.settle_ms:
+        for _ in range(10 if n_warm >= args.warmup else 1):
+            for _, fn in stages:
+                fn()
+            n_warm += 1
+        if n_warm >= args.warmup:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
 
+    def timed_steps(per_stage: bool):
+        """K steps between device synchronisations; with per_stage, an event
+        pair around every stage (each record adds a few us of launch gap)."""
+        pairs = [(name, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(args.steps) for name, _ in stages] if per_stage else []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        i = 0
+        for _ in range(args.steps):
+            if args.idle_gap_ms > 0:
+                torch.cuda.synchronize()
+                time.sleep(args.idle_gap_ms * 1e-3)
+            for name, fn in stages:
+                if per_stage:
+                    pairs[i][1].record(stream)
+                fn()
+                if per_stage:
+                    pairs[i][2].record(stream)
+                i += 1
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, pairs
+
+    # The timed region: exactly K steps, launched back to back.
+    wall, _ = timed_steps(per_stage=False)
+    ms_per_step = wall / args.steps * 1e3
+    # Per-kernel times: K more steps with events around every stage.
+    _, pairs = timed_steps(per_stage=True)
     ev = {name: [] for name, _ in stages}
-    pairs = []
-    for _ in range(args.steps):
-        for name, _ in stages:
-            pairs.append((name, torch.cuda.Event(enable_timing=True),
-                          torch.cuda.Event(enable_timing=True)))
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    i = 0
-    for _ in range(args.steps):
-        for name, fn in stages:
-            _, e0, e1 = pairs[i]
-            e0.record(stream)
-            fn()
-            e1.record(stream)
-            i += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     for name, e0, e1 in pairs:
         ev[name].append(e0.elapsed_time(e1) * 1e3)          # us
     us = {k: float(np.mean(v)) for k, v in ev.items()}
     med = {k: float(np.median(v)) for k, v in ev.items()}
-    ms_per_step = wall / args.steps * 1e3
+    if args.idle_gap_ms > 0:
+        ms_per_step = sum(med.values()) * 1e-3
 
     hbm = args.workload in HBM_BOUND
     total_bytes = work["gate_up_bytes"] + work["down_bytes"]
@@ -271,14 +302,16 @@ def main():
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "steps": args.steps, "warmup": args.warmup, "warmup_settle_ms": args.settle_ms,
+        "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload,
                    "rows": work["rows"], "weights": "uint4 group-32 bf16 scales, zero point 8",
                    "parallelism": "one EP/TP rank's share on one GPU",
                    "schedule": {"gate_up": "dynamic" if sched_applied[0] else "semi_static",
-                                "down": "dynamic" if sched_applied[1] else "semi_static"}},
+                                "down": "dynamic" if sched_applied[1] else "semi_static"},
+                   **({"idle_gap_ms": args.idle_gap_ms} if args.idle_gap_ms > 0 else {})},
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
         "kernel_us_mean": {k: round(v, 2) for k, v in us.items()},
         "kernel_us_median": {k: round(v, 2) for k, v in med.items()},

@@ -91,6 +91,16 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     if (ntw > 1 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
         L.N % (64 * (ntw / 2)) == 0)
       ntw /= 2;
+    // Between one and two workgroups per CU with long K (an EP32 gate_up
+    // share: 384 tiles), two wave pairs splitting K keep more weight loads in
+    // flight per workgroup than four waves side by side (measured 52 vs
+    // 60 us); split-K only adds a reduction there.
+    const int64_t t128 = L.N % 128 == 0 ? (int64_t)tiles_m * (L.N / 128) : 0;
+    if (tm == 1 && L.k_chunks >= 4 * qma::kStreamChunks && t128 >= qma::kNumCUs &&
+        t128 < 2 * qma::kNumCUs) {
+      wk = 2;
+      ntw = 4;
+    }
   } else {
     // 64-row tiles: the four waves split K in two when K is long (each wave
     // still streams >= 12 chunks of 128) and split the columns otherwise.
@@ -125,8 +135,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->split_k = split;
   // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
   // chunks in flight per wave at three workgroups per CU
-  p->k_depth = (tm <= 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw)) *
-               qma::kChunkK;
+  int depth = tm <= 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw);
+  if (tm == 1 && wk == 2 && split == 1) depth = 4;  // the K-split pairs above
+  p->k_depth = depth * qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
   // only one or two chunks would spend its life on start-up and one memory
   // round trip. It streams several N blocks of its expert through the same

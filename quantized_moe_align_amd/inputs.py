@@ -23,6 +23,7 @@ hidden 7168, intermediate 2048, 384 experts, top-8):
 * ``ep8_prefill_span`` the same row total with counts spanning ~590..20.
 * ``contiguous``  48 experts x 128 rows, grouped_contiguous layout.
 * ``masked``      48 experts, 64-row budget, 32 valid rows each.
+* ``ep16_decode`` 24 local experts, counts U{9..15} (EP16 rank share).
 * ``ep32_decode`` 12 local experts, counts U{9..15} (split-K gate probe).
 """
 from __future__ import annotations
@@ -213,7 +214,7 @@ def make_masked(name, seed, E, budget, valid, K, I, expected_m=None,
 
 
 WORKLOADS = ("tiny", "ep8_decode", "tp8", "ep8_prefill", "ep8_prefill_span",
-             "contiguous", "masked", "ep32_decode")
+             "contiguous", "masked", "ep16_decode", "ep32_decode")
 
 
 def make(name: str, seed: int = 0, weights: bool = True,
@@ -228,6 +229,9 @@ def make(name: str, seed: int = 0, weights: bool = True,
                                     128 if I == INTER else I, weights)
     if name == "ep8_decode":
         return make_count_workload(name, seed, uniform_counts(seed, 48), K, I,
+                                   weights, {"routing": "U{9..15} per expert"})
+    if name == "ep16_decode":
+        return make_count_workload(name, seed, uniform_counts(seed, 24), K, I,
                                    weights, {"routing": "U{9..15} per expert"})
     if name == "ep32_decode":
         return make_count_workload(name, seed, uniform_counts(seed, 12), K, I,

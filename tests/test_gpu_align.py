@@ -41,7 +41,7 @@ def check(ids, E, B, extra=0):
 
 @pytest.mark.parametrize("name,B", [("tiny", 16), ("tiny", 32), ("ep8_decode", 16),
                                     ("tp8", 16), ("ep8_prefill", 64), ("ep8_prefill", 128),
-                                    ("ep32_decode", 16), ("ep8_prefill_span", 128)])
+                                    ("ep16_decode", 16), ("ep32_decode", 16), ("ep8_prefill_span", 128)])
 def test_workload_routing_bit_exact(gpu, name, B):
     wl = inputs.make(name, seed=0, weights=False)
     check(wl["topk_ids"], wl.E, B, extra=3 * B + 5)

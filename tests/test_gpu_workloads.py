@@ -55,7 +55,7 @@ def check_stages(a_bits, a_row_div, slot_expert, c1, h, c2, w13, s13, w2, s2, rn
     assert_per_expert(c2[cs][:, cols2], ref_chain[cs], sc[cs], f"{what} chained")
 
 
-@pytest.mark.parametrize("name", ["ep8_decode", "tp8", "ep8_prefill", "ep32_decode",
+@pytest.mark.parametrize("name", ["ep8_decode", "tp8", "ep8_prefill", "ep16_decode", "ep32_decode",
                                   "ep8_prefill_span"])
 def test_indexed_workload(gpu, name):
     wl = inputs.make(name, seed=0)

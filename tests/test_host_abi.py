@@ -122,9 +122,15 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
     # 4 experts: the 64-column width gives exactly 256 tiles -> no split
     assert _plan(4, 4096, 7168, 48, 1).split_k == 1
-    # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> full width, no split
+    # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> no split; between one
+    # and two workgroups per CU the waves split K in pairs (128 columns)
     q = _plan(12, 4096, 7168, 144, 1)
-    assert q.split_k == 1 and q.block_n == 128
+    assert q.split_k == 1 and q.block_n == 128 and q.waves_k == 2 and q.k_depth == 512
+    # EP32 down (672 tiles) and EP16 gate_up (768 tiles): four waves side by side
+    d = _plan(12, 7168, 2048, 144, 1)
+    assert d.split_k == 1 and d.block_n == 128 and d.waves_k == 1
+    g = _plan(24, 4096, 7168, 288, 1)
+    assert g.split_k == 1 and g.block_n == 128 and g.waves_k == 1
 
 
 def test_stream_rule():
