@@ -305,6 +305,42 @@ LARGE_SHAPES = [  # (E, T, topk, K, N): >= 80 rows per expert
 ]
 
 
+# expert row counts on both sides of the 64-row boundary of a 128-row tile:
+# tiles whose tokens all sit in rows 0..63 take the half-tile launch
+HALF_TILE_COUNTS = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 0, 256]
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_large_m_half_tiles_bitwise(gpu, split):
+    E, K, N = len(HALF_TILE_COUNTS), 512, 256
+    rng = np.random.default_rng(70 + split)
+    w, s = weights(rng, E, N, K, integer=True)
+    ids = np.repeat(np.arange(E, dtype=np.int32), HALF_TILE_COUNTS)
+    ids = rng.permutation(ids)[:, None]
+    a = bf16_small_ints(rng, (ids.shape[0], K))
+    got, plan = indexed(a, 1, ids, w, s, force_bm=128, override={"split_k": split})
+    assert plan.kernel == qma.KERNEL_LARGE_M and plan.split_k == split
+    ref = O.moe_gemm_by_slot(a, 1, ids, w, s)
+    assert np.array_equal(got, rne(ref))
+
+
+@pytest.mark.parametrize("split", [1, 2])
+def test_large_m_masked_half_tiles_bitwise(gpu, split):
+    E, Mb, K, N = 6, 256, 256, 256
+    rng = np.random.default_rng(80 + split)
+    masked_m = np.array([0, 1, 64, 65, 129, 256], np.int32)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (E, Mb, K))
+    large = {"kernel": qma.KERNEL_LARGE_M, "block_m": 128, "block_n": 256, "waves_k": 1,
+             "split_k": split}
+    got = masked(a, masked_m, 128, w, s, large)
+    ref = O.grouped_masked(a, masked_m, w, s)
+    for e in range(E):
+        m = masked_m[e]
+        assert np.array_equal(got[e, :m], rne(ref[e, :m])), e
+        assert np.all(got[e, m:] == SENT), e
+
+
 @pytest.mark.parametrize("shape", LARGE_SHAPES)
 def test_large_m_integer_exact_bitwise(gpu, shape):
     E, T, topk, K, N = shape
