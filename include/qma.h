@@ -180,7 +180,9 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * block_n comes from the tile count ([release] grouped techniques: the
  * wider tile only when enough N tiles exist), and split-K turns on only
  * when the grid would underfill the compute units ([release] indexed
- * techniques: the stream-K gate). force_block_m = 0 lets the planner choose;
+ * techniques: the stream-K gate). Between one and two workgroups per compute
+ * unit with long K, 16-row tiles split K across wave pairs inside the
+ * workgroup (waves_k = 2) instead. force_block_m = 0 lets the planner choose;
  * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128
  * the large-M kernel (which needs N % 256 == 0). The down projection passes
  * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,
