@@ -154,6 +154,46 @@ def cpu_baseline(wl, budget_s):
     return t_total, done_bytes, done_flops, threads, experts
 
 
+def practical_roofs(torch, dev):
+    """What plain reference work reaches on this GPU, next to the vendor
+    peaks: a 1 GiB device copy (torch's copy kernel; read + write bytes) and a
+    dense 8192^3 bf16 matmul (the vendor GEMM library through torch). Both are
+    measured after the timed region, back to back with a settle, and serve as
+    context only; neither is on the product path."""
+    import time as _t
+
+    def run(fn, n):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = _t.perf_counter()
+        while _t.perf_counter() - t0 < 0.2:
+            fn()
+            torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / n                  # s per call
+
+    nbytes = 1 << 30
+    src = torch.empty(nbytes // 4, dtype=torch.int32, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    t_copy = run(lambda: dst.copy_(src), 20)
+    del src, dst
+    n = 8192
+    a = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
+    t_mm = run(lambda: torch.mm(a, b), 10)
+    del a, b
+    return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "dense_bf16_gemm_TFLOPs": round(2 * n ** 3 / t_mm / 1e12, 1),
+            "note": "1 GiB device copy (read + write); dense 8192^3 bf16 matmul via torch"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -174,6 +214,8 @@ def main():
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="continue the untimed warm-up until the step has run back to "
                          "back for this long (clock ramp from idle)")
+    ap.add_argument("--no-roofs", dest="roofs", action="store_false",
+                    help="skip the practical-roof measurements (device copy, dense bf16 GEMM)")
     ap.add_argument("--idle-gap-ms", type=float, default=0.0,
                     help="idle the GPU this long before each timed step (untimed), to "
                          "compare isolated launches with the sustained back-to-back "
@@ -324,6 +366,8 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
     }
+    if args.roofs:
+        out["practical_roofs"] = practical_roofs(torch, dev)
     if args.copy_bytes > 0:
         src = torch.empty(args.copy_bytes // 4, dtype=torch.int32, device=dev).fill_(1)
         dst = torch.empty_like(src)
