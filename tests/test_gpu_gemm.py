@@ -79,16 +79,22 @@ def test_indexed_random_within_tolerance(gpu, shape, force_bm):
     assert_per_expert(got, ref, slot_experts(ids, E), f"{shape} bm={plan.block_m}")
 
 
-@pytest.mark.parametrize("shape", SHAPES)
-@pytest.mark.parametrize("force_bm,ntw,wk", [(0, 0, 0), (16, 1, 4), (16, 2, 1), (16, 4, 2),
-                                             (16, 4, 4), (16, 4, 1), (32, 4, 4), (32, 2, 2),
-                                             (32, 1, 1), (32, 4, 1), (32, 2, 1), (64, 2, 4),
-                                             (64, 1, 2)])
+KERNEL_INSTANCES = [(0, 0, 0), (16, 1, 4), (16, 2, 1), (16, 4, 2), (16, 4, 4), (16, 4, 1),
+                    (32, 4, 4), (32, 2, 2), (32, 1, 1), (32, 4, 1), (32, 2, 1), (64, 2, 4),
+                    (64, 1, 2)]                       # (force_bm, ntw, waves_k); 0 = planner
+
+
+def _fits(shape, inst):
+    _, ntw, wk = inst
+    return not ntw or shape[4] % (ntw * 16 * (4 // wk)) == 0
+
+
+@pytest.mark.parametrize("shape,force_bm,ntw,wk",
+                         [(sh,) + inst for sh in SHAPES for inst in KERNEL_INSTANCES
+                          if _fits(sh, inst)])
 def test_indexed_integer_exact_bitwise(gpu, shape, force_bm, ntw, wk):
     E, T, topk, K, N = shape
     block_n = ntw * 16 * (4 // wk) if ntw else 0
-    if block_n and N % block_n:
-        pytest.skip("width does not divide N")
     rng = np.random.default_rng(7 + E + T)
     w, s = weights(rng, E, N, K, integer=True)
     a = bf16_small_ints(rng, (T, K))
