@@ -218,7 +218,8 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "plan has bad schedule %d", plan->schedule);
   if (plan->n_stream < 1 || plan->n_stream > 64 ||
       (plan->n_stream > 1 && (plan->kernel != QMA_KERNEL_SMALL_M || plan->waves_k != 1 ||
-                              plan->split_k != 1 || plan->block_m != 16)))
+                              plan->split_k != 1 || plan->block_m != 16 ||
+                              (plan->block_n != 128 && plan->block_n != 256))))
     return fail(QMA_ERR_INVALID_ARG, "plan has bad n_stream %d", plan->n_stream);
   if (plan->block_n != 16 && plan->block_n != 32 && plan->block_n != 64 &&
       plan->block_n != 128 && plan->block_n != 256)
@@ -226,6 +227,16 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
   if (L.N % plan->block_n != 0)
     return fail(QMA_ERR_INVALID_ARG, "block_n %d does not divide N %d",
                 plan->block_n, L.N);
+  if (plan->kernel == QMA_KERNEL_SMALL_M) {
+    // the small-M kernel instances: 16-column tiles per wave (ntw) times the
+    // waves side by side (4 / waves_k)
+    const int wk = plan->waves_k;
+    const int wn = (wk == 1 || wk == 2 || wk == 4) ? 4 / wk : 0;
+    if (!wn || plan->block_n % (16 * wn) != 0 ||
+        !qma::small_m_supported(plan->block_m / 16, plan->block_n / (16 * wn)))
+      return fail(QMA_ERR_INVALID_ARG, "no small-M kernel for a %d x %d block with waves_k %d",
+                  plan->block_m, plan->block_n, wk);
+  }
   return ok();
 }
 

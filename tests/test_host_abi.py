@@ -229,6 +229,19 @@ def test_host_checks_before_any_launch(L):
         with pytest.raises(qma.QmaError) as e7:           # misaligned packed weights
             qma.qma_prepack(lay, fake, fake, fake + 4, stream=0)
         assert e7.value.status == qma.QMA_ERR_INVALID_ARG
+        # edited plans naming no kernel instance: 8 column tiles per wave,
+        # waves_k 3, a streamed 64-column block
+        for edit in ({"block_m": 16, "block_n": 128, "waves_k": 4, "split_k": 1},
+                     {"block_m": 16, "block_n": 128, "waves_k": 3, "split_k": 1},
+                     {"block_m": 64, "block_n": 256, "waves_k": 1, "split_k": 1},
+                     {"block_m": 16, "block_n": 64, "waves_k": 1, "split_k": 1, "n_stream": 2}):
+            q = qma.Plan.from_buffer_copy(qma.qma_plan_indexed(lay, 64, 2))
+            for k, v in edit.items():
+                setattr(q, k, v)
+            with pytest.raises(qma.QmaError) as e8:
+                qma.qma_indexed_gemm(lay, q, fake, 64, 2, fake, fake, fake, fake, cap, 128,
+                                     None, fake, stream=0)
+            assert e8.value.status == qma.QMA_ERR_INVALID_ARG, edit
     finally:
         qma.qma_layer_destroy(lay)
         qma.qma_layer_destroy(other)
