@@ -54,6 +54,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 // ---------------------------------------------------------------------------
 constexpr int kAlignWaves = 8;
 constexpr int kAlignThreads = kAlignWaves * 64;
+constexpr int kAlignUnroll = 8;   // ids each lane loads before using any
 
 __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
     const int32_t* __restrict__ ids, int32_t R, int32_t E, int32_t B,
@@ -70,9 +71,19 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
   __syncthreads();
   const int per = (R + kAlignWaves - 1) / kAlignWaves;
   const int lo = min(R, w * per), hi = min(R, lo + per);
-  for (int i = lo + lane; i < hi; i += 64) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&wc[w * E + e], 1);
+  // the ids of kAlignUnroll rows of 64 slots are loaded together, so a
+  // wave waits out one memory round trip per batch rather than per row
+  constexpr int U = kAlignUnroll;
+  for (int base = lo; base < hi; base += 64 * U) {
+    int ev[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base + u * 64 + lane;
+      ev[u] = i < hi ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&wc[w * E + ev[u]], 1);
   }
   __syncthreads();
   // per expert: total, and exclusive prefix over waves (in place)
@@ -126,28 +137,48 @@ __global__ __launch_bounds__(kAlignThreads) void moe_align_kernel(
     expert_ids[b] = e;
   }
   // sentinel padding inside each expert's segment, and the tail
-  for (int e = tid; e < E; e += kAlignThreads)
-    for (int p = off[e] + cnt[e]; p < off[e + 1]; ++p) sorted_ids[p] = R;
+  // (large blocks: one wave per expert, its lanes over the up to B - 1
+  // padding positions; small blocks: one thread per expert)
+  if (B >= 64) {
+    for (int e = w; e < E; e += kAlignWaves)
+      for (int p = off[e] + cnt[e] + lane; p < off[e + 1]; p += 64) sorted_ids[p] = R;
+  } else {
+    for (int e = tid; e < E; e += kAlignThreads)
+      for (int p = off[e] + cnt[e]; p < off[e + 1]; ++p) sorted_ids[p] = R;
+  }
   for (int p = ntp + tid; p < cap; p += kAlignThreads) sorted_ids[p] = R;
   __syncthreads();
-  // pass 2: place each slot
+  // pass 2: place each slot; lanes of a row holding the same expert are
+  // found with one ballot per bit of the expert index
   const int nbits = E > 1 ? 32 - __clz(E - 1) : 1;
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int base = lo; base < hi; base += 64) {
-    const int i = base + lane;
-    const int e = (i < hi) ? ids[i] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t peers = __ballot(valid);
-    for (int bit = 0; bit < nbits; ++bit) {
-      const bool set = valid && ((e >> bit) & 1);
-      const uint64_t m = __ballot(set);
-      peers &= set ? m : ~m;
+  for (int base0 = lo; base0 < hi; base0 += 64 * U) {
+    int ev[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int i = base0 + u * 64 + lane;
+      ev[u] = i < hi ? ids[i] : -1;
     }
-    const int rank = __popcll(peers & below);
-    int pos = 0;
-    if (valid) pos = wc[w * E + e];
-    if (valid) sorted_ids[pos + rank] = i;
-    if (valid && (peers & below) == 0) wc[w * E + e] = pos + __popcll(peers);
+    // rows in slot order, so each expert's slots stay ascending
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int base = base0 + u * 64;
+      if (base >= hi) break;
+      const int i = base + lane;
+      const int e = ev[u];
+      const bool valid = (unsigned)e < (unsigned)E;
+      uint64_t peers = __ballot(valid);
+      for (int bit = 0; bit < nbits; ++bit) {
+        const bool set = valid && ((e >> bit) & 1);
+        const uint64_t m = __ballot(set);
+        peers &= set ? m : ~m;
+      }
+      const int rank = __popcll(peers & below);
+      int pos = 0;
+      if (valid) pos = wc[w * E + e];
+      if (valid) sorted_ids[pos + rank] = i;
+      if (valid && (peers & below) == 0) wc[w * E + e] = pos + __popcll(peers);
+    }
   }
 }
 
