@@ -100,7 +100,14 @@ typedef enum qma_kernel {
  * counts ([announce] scheduling section: the schedule follows the routed
  * tokens per expert, not the total; profile and layout are fixed at load
  * and the token count only tunes the schedule within them). Every field is
- * plain data so tests can check the rules. */
+ * plain data so tests can check the rules. A caller may edit kernel,
+ * block_m, block_n, split_k, k_depth, waves_k, n_stream and schedule; the
+ * GEMM calls validate the plan against the layer and reject, with
+ * QMA_ERR_INVALID_ARG and before any launch, a plan made for another layer
+ * or one that names no compiled kernel instance (small-M: block_m in
+ * {16, 32, 64}, waves_k in {1, 2, 4}, at most 8 16x16 tiles per wave;
+ * large-M: a 128 x 256 block). k_depth outside an instance's supported
+ * depths falls back to that instance's default. */
 typedef struct qma_plan {
   int32_t path;          /* qma_path of the layer */
   int32_t kernel;        /* qma_kernel */
