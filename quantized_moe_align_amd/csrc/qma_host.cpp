@@ -190,6 +190,21 @@ qma_status check_a_bytes(int64_t rows, int32_t K) {
   return ok();
 }
 
+// The semi-static grid covers every (tile, column block, split) the host
+// can bound: the tile count padded to the 8 XCDs, times the column blocks
+// one workgroup does not stream, times the splits. Workgroup indices must
+// stay below 2^24.
+qma_status check_grid(int64_t num_tiles, const qma_plan_t* plan) {
+  const int64_t tiles_pad = (num_tiles + 7) / 8 * 8;
+  const int64_t nblocks = plan->n / plan->block_n;
+  const int64_t per = (nblocks + plan->n_stream - 1) / plan->n_stream;
+  if (tiles_pad * per * plan->split_k >= (1ll << 24))
+    return fail(QMA_ERR_INVALID_ARG, "%lld tiles x %lld column blocks x %d splits exceed "
+                "2^24 workgroups; split the call", (long long)num_tiles, (long long)per,
+                plan->split_k);
+  return ok();
+}
+
 qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
                             int32_t path) {
   if (!layer || !plan) return fail(QMA_ERR_INVALID_ARG, "null layer or plan");
@@ -554,6 +569,8 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
   if ((s = check_ws(plan, num_slots, ws, ws_bytes)) != QMA_OK) return s;
   if ((s = check_a_bytes(a_rows, layer->L.K)) != QMA_OK) return s;
+  if ((s = check_grid(((int64_t)sorted_cap + plan->block_m - 1) / plan->block_m, plan)) != QMA_OK)
+    return s;
   if (sorted_cap == 0 || num_slots == 0) return ok();
   qma::GemmArgs g{};
   g.layer = &layer->L;
@@ -591,6 +608,7 @@ qma_status qma_grouped_contiguous_gemm(const qma_layer_t* layer, const qma_plan_
     return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
   if ((s = check_ws(plan, M, ws, ws_bytes)) != QMA_OK) return s;
   if ((s = check_a_bytes(M, layer->L.K)) != QMA_OK) return s;
+  if ((s = check_grid(M / plan->block_m, plan)) != QMA_OK) return s;
   if (M == 0) return ok();
   qma::GemmArgs g{};
   g.layer = &layer->L;
@@ -625,6 +643,9 @@ qma_status qma_grouped_masked_gemm(const qma_layer_t* layer, const qma_plan_t* p
     return fail(QMA_ERR_INVALID_ARG, "a/c must be 16-byte and packed_w 256-byte aligned");
   if ((s = check_ws(plan, (int64_t)Mb * layer->L.E, ws, ws_bytes)) != QMA_OK) return s;
   if ((s = check_a_bytes((int64_t)Mb * layer->L.E, layer->L.K)) != QMA_OK) return s;
+  if ((s = check_grid((int64_t)(Mb + plan->block_m - 1) / plan->block_m * layer->L.E, plan)) !=
+      QMA_OK)
+    return s;
   qma::GemmArgs g{};
   g.layer = &layer->L;
   g.plan = plan;
