@@ -229,12 +229,13 @@ def test_host_checks_before_any_launch(L):
         with pytest.raises(qma.QmaError) as e7:           # misaligned packed weights
             qma.qma_prepack(lay, fake, fake, fake + 4, stream=0)
         assert e7.value.status == qma.QMA_ERR_INVALID_ARG
+        p0 = qma.qma_plan_indexed(lay, 64, 2)            # unsplit: no workspace
         with pytest.raises(qma.QmaError) as e9:           # 2 GiB of activations
-            qma.qma_indexed_gemm(lay, p, fake, 1 << 22, 2, fake, fake, fake, fake, cap, 128,
+            qma.qma_indexed_gemm(lay, p0, fake, 1 << 22, 2, fake, fake, fake, fake, cap, 128,
                                  None, fake, stream=0)
         assert e9.value.status == qma.QMA_ERR_INVALID_ARG
         with pytest.raises(qma.QmaError) as e10:          # grid beyond 2^24 workgroups
-            qma.qma_indexed_gemm(lay, p, fake, 64, 2, fake, fake, fake, fake, 1 << 30, 128,
+            qma.qma_indexed_gemm(lay, p0, fake, 64, 2, fake, fake, fake, fake, 1 << 30, 128,
                                  None, fake, stream=0)
         assert e10.value.status == qma.QMA_ERR_INVALID_ARG
         # edited plans naming no kernel instance: 8 column tiles per wave,
