@@ -1,6 +1,7 @@
 // HIP kernels of libqma for gfx950 (CDNA4): block-aligned routing
 // (moe_align), weight prepack, the W4A16 expert GEMMs, the split-K
-// reduction, the SiLU-gated activation and the top-k combine.
+// reduction, the SiLU-gated activation, the top-k combine and the router's
+// top-k softmax.
 //
 // The passages followed are cited per kernel (page titles in include/qma.h).
 #include <hip/hip_runtime.h>
