@@ -386,6 +386,17 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 constexpr int kBufWord3 = 0x00020000;  // raw 32-bit buffer resource, gfx9 family
 constexpr int kNonTemporal = 2;        // streaming load: weights are read once
 
+// A pointer the compiler may not prove wave-uniform, made so (every lane
+// holds the same value): a buffer resource built from it then stays in
+// scalar registers instead of needing a loop over lanes per load.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* q) {
+  const uint64_t v = (uint64_t)(uintptr_t)q;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            kBufWord3);
@@ -1132,16 +1143,20 @@ __device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
 }
 
 
+// Rows of a tile that hold no token are never computed: the tile's valid
+// rows are counted first, and only the 32-row groups that hold any of them
+// are loaded, multiplied and stored (a 128-row tile that ends an expert's
+// rows typically holds fewer than 128). Each count of groups has its own
+// copy of the main loop.
 __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p) {
   constexpr int BM = kLmBM;
-  constexpr int ROWS_W = BM / 4;           // token rows each wave copies per chunk
-  constexpr int NA = ROWS_W / 4;           // direct-to-LDS loads per lane per chunk
   // Token-tile LDS buffers: two separate objects, so the compiler's wait
   // counts can tell a load into one buffer from a read of the other.
   __shared__ __attribute__((aligned(1024))) uint8_t s_a0[BM * kLmRowBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t s_a1[BM * kLmRowBytes];
   __shared__ int32_t s_arow[BM];
   __shared__ int32_t s_out[BM];
+  __shared__ int32_t s_rows;   // one past the tile's last valid row
 
   int tile, nb, sp;
   if (!decode_bid_lm(p, tile, nb, sp)) return;
@@ -1151,12 +1166,16 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int c16 = lane & 15, kq = lane >> 5, l32 = lane & 31;
 
+  if (threadIdx.x == 0) s_rows = 0;
+  __syncthreads();
   for (int r = threadIdx.x; r < BM; r += 256) {
     const RowInfo ri = row_info(p, tile, e, r);
     s_arow[r] = ri.valid ? ri.a_row : -1;
     s_out[r] = ri.valid ? ri.out_row : -1;
+    if (ri.valid) atomicMax(&s_rows, r + 1);
   }
   __syncthreads();
+  const int groups = __builtin_amdgcn_readfirstlane((s_rows + 31) >> 5);
 
   const int c0 = (int)(((int64_t)sp * p.KC) / p.split);
   const int c1 = (int)(((int64_t)(sp + 1) * p.KC) / p.split);
@@ -1165,228 +1184,251 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
   // so every step issues the same loads and the wait counts stay exact
   auto chunk = [&](int j) { return c0 + min(j, n - 1); };
 
-  // Token rows: wave w copies rows w*ROWS_W .. +ROWS_W-1, four rows (one
-  // per 16-lane group) per instruction; lane l lands in slot l % 16 of its
-  // row, which holds the row's segment (l % 16) ^ (row % 16).
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-  uint32_t voff_a[NA];
-#pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int row = w * ROWS_W + 4 * i + (lane >> 4);
-    const int ar = s_arow[row];
-    const uint32_t seg = (uint32_t)(c16 ^ (row & 15));
-    voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
-  }
-  // (the LDS address is formed from the __shared__ array itself, which the
-  // host compilation pass can type-check)
-  auto load_a = [&](auto buf_id, int c) {
-#pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int off = (w * ROWS_W + 4 * i) * kLmRowBytes;
-      const int vo = (int)voff_a[i];
-      if constexpr (decltype(buf_id)::value == 0)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(s_a0 + off), 16, vo,
-            c * kLmRowBytes, 0, 0);
-      else
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ra, (__attribute__((address_space(3))) void*)(s_a1 + off), 16, vo,
-            c * kLmRowBytes, 0, 0);
-    }
-  };
-  using B0 = std::integral_constant<int, 0>;
-  using B1 = std::integral_constant<int, 1>;
-
   // Weights: this wave's 64 columns are 16-column packed tiles nt16..+3;
   // 32-column tile t uses packed tiles 2t and 2t+1.
   const int nt16 = nb * (kLmBN / 16) + w * 4;
   const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
-  const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(p.wpk + ((size_t)e * p.NT + nt16) * tile_bytes, 4 * tile_bytes);
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(
+      uniform_ptr(p.wpk + ((size_t)e * p.NT + nt16) * tile_bytes), 4 * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.spk + ((size_t)e * p.NT + nt16) * p.KC * kSBlockBytes,
+      make_rsrc(uniform_ptr(p.spk + ((size_t)e * p.NT + nt16) * p.KC * kSBlockBytes),
                 4 * p.KC * kSBlockBytes);
   const int half16 = (lane >> 4) & 1;  // which 16-column tile of the 32
   const uint32_t voff_w = half16 * tile_bytes + (uint32_t)(c16 + 16 * kq) * 16u;
   const uint32_t voff_s = half16 * p.KC * kSBlockBytes + c16 * 8;
-  struct BStage {
-    u32x4 w[kLmNT][2];  // [32-column tile][K half]: one word per 32-row group
-    u32x2 s[kLmNT];     // four group scales of the lane's column
-  };
-  auto load_b = [&](BStage& b, int c) {
-#pragma unroll
-    for (int t = 0; t < kLmNT; ++t)
-#pragma unroll
-      for (int h = 0; h < 2; ++h)
-        b.w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(
-            rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, 0);
-#pragma unroll
-    for (int t = 0; t < kLmNT; ++t)
-      b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
-                                                    (2 * t * p.KC + c) * kSBlockBytes, 0);
-  };
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(uniform_ptr(p.a), p.a_bytes);
 
-  f32x16 acc[kLmMT][kLmNT];
-#pragma unroll
-  for (int mt = 0; mt < kLmMT; ++mt)
-#pragma unroll
-    for (int t = 0; t < kLmNT; ++t) acc[mt][t] = f32x16{};
+  // The main loop and epilogue for a tile whose valid rows lie in its first
+  // MT groups of 32.
+  auto body = [&](auto mt_c) {
+    constexpr int MT = decltype(mt_c)::value;  // 32-row groups computed
+    constexpr int BMA = 32 * MT;               // rows loaded and computed
+    constexpr int ROWS_W = BMA / 4;            // token rows each wave copies per chunk
+    constexpr int NA = ROWS_W / 4;             // direct-to-LDS loads per lane per chunk
+    // VALU work per K step is about 45 instructions whatever MT is; the
+    // scheduling pattern spreads it over the step's 2 MT MFMAs.
+    constexpr int VPM = MT == 4 ? 5 : (46 + 2 * MT - 1) / (2 * MT);
 
-  // One chunk: 8 K steps of 16; step ks uses group g = ks / 2, half ks % 2.
-  // Software-pipelined one step deep: the token fragments and dequantised
-  // weights of step ks+1 are fetched and computed while step ks's MFMAs run,
-  // so a wave alone on its SIMD does not wait out LDS latency.
-  auto compute = [&](const uint8_t* abuf, const BStage& b) {
-    auto frags = [&](u32x4 (&av)[kLmMT], int ks) {
+    // Token rows: wave w copies rows w*ROWS_W .. +ROWS_W-1, four rows (one
+    // per 16-lane group) per instruction; lane l lands in slot l % 16 of its
+    // row, which holds the row's segment (l % 16) ^ (row % 16).
+    uint32_t voff_a[NA];
 #pragma unroll
-      for (int mt = 0; mt < kLmMT; ++mt) {
-        const int row = mt * 32 + l32;
-        const int slot = (2 * ks + kq) ^ (row & 15);
-        av[mt] = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
+    for (int i = 0; i < NA; ++i) {
+      const int row = w * ROWS_W + 4 * i + (lane >> 4);
+      const int ar = s_arow[row];
+      const uint32_t seg = (uint32_t)(c16 ^ (row & 15));
+      voff_a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
+    }
+    // (the LDS address is formed from the __shared__ array itself, which the
+    // host compilation pass can type-check)
+    auto load_a = [&](auto buf_id, int c) {
+#pragma unroll
+      for (int i = 0; i < NA; ++i) {
+        const int off = (w * ROWS_W + 4 * i) * kLmRowBytes;
+        const int vo = (int)voff_a[i];
+        if constexpr (decltype(buf_id)::value == 0)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ra, (__attribute__((address_space(3))) void*)(s_a0 + off), 16, vo,
+              c * kLmRowBytes, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              ra, (__attribute__((address_space(3))) void*)(s_a1 + off), 16, vo,
+              c * kLmRowBytes, 0, 0);
       }
     };
-    auto deq = [&](u32x4 (&bw)[kLmNT], int ks) {
-      const int g = ks >> 1, h = ks & 1;
-#pragma unroll
-      for (int t = 0; t < kLmNT; ++t) {
-        const uint32_t sw = b.s[t][g >> 1];
-        const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        bw[t] = dequant8(b.w[t][h][g], sc, -8.0f * sc);
-      }
+    using B0 = std::integral_constant<int, 0>;
+    using B1 = std::integral_constant<int, 1>;
+
+    struct BStage {
+      u32x4 w[kLmNT][2];  // [32-column tile][K half]: one word per 32-row group
+      u32x2 s[kLmNT];     // four group scales of the lane's column
     };
-    u32x4 av[2][kLmMT], bw[2][kLmNT];
-    frags(av[0], 0);
-    deq(bw[0], 0);
+    auto load_b = [&](BStage& b, int c) {
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const int cur = ks & 1;
-      if (ks < 7) {
-        frags(av[cur ^ 1], ks + 1);
-        deq(bw[cur ^ 1], ks + 1);
-      }
+      for (int t = 0; t < kLmNT; ++t)
 #pragma unroll
-      for (int mt = 0; mt < kLmMT; ++mt)
+        for (int h = 0; h < 2; ++h)
+          b.w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(
+              rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, 0);
 #pragma unroll
-        for (int t = 0; t < kLmNT; ++t) acc[mt][t] = mfma32(av[cur][mt], bw[cur][t], acc[mt][t]);
-      if (ks < 7) {
-        // next step's fragment reads first, then each MFMA followed by a
-        // share of the next step's dequantisation
-        __builtin_amdgcn_sched_group_barrier(0x100, kLmMT, 0);
+      for (int t = 0; t < kLmNT; ++t)
+        b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
+                                                      (2 * t * p.KC + c) * kSBlockBytes, 0);
+    };
+
+    f32x16 acc[MT][kLmNT];
 #pragma unroll
-        for (int i = 0; i < kLmMT * kLmNT; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int t = 0; t < kLmNT; ++t) acc[mt][t] = f32x16{};
+
+    // One chunk: 8 K steps of 16; step ks uses group g = ks / 2, half ks % 2.
+    // Software-pipelined one step deep: the token fragments and dequantised
+    // weights of step ks+1 are fetched and computed while step ks's MFMAs
+    // run, so a wave alone on its SIMD does not wait out LDS latency.
+    auto compute = [&](const uint8_t* abuf, const BStage& b) {
+      auto frags = [&](u32x4 (&av)[MT], int ks) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int row = mt * 32 + l32;
+          const int slot = (2 * ks + kq) ^ (row & 15);
+          av[mt] = *(const u32x4*)(abuf + row * kLmRowBytes + slot * 16);
         }
-      }
-    }
-  };
-
-  // Issue order per step j: [wait, barrier] token rows of chunk j+1 (into
-  // the buffer chunk j-1 used), compute chunk j, weights of chunk j+2.
-  // Chunk j's token rows are therefore followed by exactly chunk j+1's
-  // weights (kLmBLoads loads) when step j waits for them.
-  BStage bs0, bs1;
-  load_b(bs0, chunk(0));
-  load_a(B0{}, chunk(0));
-  __builtin_amdgcn_sched_barrier(0);
-  load_b(bs1, chunk(1));
-  // step on chunk j: `cur` is j's buffer (0 or 1), the other gets chunk j+1.
-  // The last step waits for everything, since the count of loads issued
-  // after its token rows is not fixed there.
-  auto step = [&](int j, auto cur, BStage& b) {
-    if (j + 1 < n)
-      wait_vmcnt<kLmBLoads>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    // (sched barriers keep the weight prefetch behind the token-row loads)
-    if constexpr (decltype(cur)::value == 0) {
-      load_a(B1{}, chunk(j + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(&s_a0[0], b);
-    } else {
-      load_a(B0{}, chunk(j + 1));
-      __builtin_amdgcn_sched_barrier(0);
-      compute(&s_a1[0], b);
-    }
-    load_b(b, chunk(j + 2));
-  };
-  for (int j = 0;; j += 2) {
-    step(j, B0{}, bs0);
-    if (j + 1 >= n) break;
-    step(j + 1, B1{}, bs1);
-    if (j + 2 >= n) break;
-  }
-  wait_vmcnt<0>();
-
-  // Output. Accumulator element 4i + r of tile (mt, t) is token
-  // 32 mt + 8 i + 4 (l/32) + r, column 32 t + l % 32 of the wave's 64; direct
-  // stores would be 2-byte scatters. The tile goes through the two token
-  // buffers instead (free once every wave is past its last read), then out
-  // in full rows with 16-byte stores. Staged row R keeps its 16-byte unit u
-  // at u ^ (R % 16), so the accumulator-layout writes (rows 4 apart) and the
-  // row-major reads both fall in distinct banks.
-  __syncthreads();
-  if (p.split == 1) {
-    // bf16 tile: BM rows of 256 columns (512 bytes), rows 0..63 in s_a0
+      };
+      auto deq = [&](u32x4 (&bw)[kLmNT], int ks) {
+        const int g = ks >> 1, h = ks & 1;
 #pragma unroll
-    for (int mt = 0; mt < kLmMT; ++mt)
+        for (int t = 0; t < kLmNT; ++t) {
+          const uint32_t sw = b.s[t][g >> 1];
+          const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+          bw[t] = dequant8(b.w[t][h][g], sc, -8.0f * sc);
+        }
+      };
+      u32x4 av[2][MT], bw[2][kLmNT];
+      frags(av[0], 0);
+      deq(bw[0], 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int ks = 0; ks < 8; ++ks) {
+        const int cur = ks & 1;
+        if (ks < 7) {
+          frags(av[cur ^ 1], ks + 1);
+          deq(bw[cur ^ 1], ks + 1);
+        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int R = mt * 32 + 8 * i + 4 * kq + r;
-          const int out = s_out[R];
-          const float tw = (p.mode == 0 && p.topk_w && out >= 0) ? p.topk_w[out] : 1.0f;
-          uint8_t* row = mt < kLmMT / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+        for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int t = 0; t < kLmNT; ++t) {
-            const int C = w * 64 + t * 32 + l32;
-            *(uint16_t*)(row + (((C >> 3) ^ (R & 15)) << 4) + (C & 7) * 2) =
-                (uint16_t)(cvt_pk_bf16(acc[mt][t][4 * i + r] * tw, 0.f) & 0xFFFFu);
+          for (int t = 0; t < kLmNT; ++t)
+            acc[mt][t] = mfma32(av[cur][mt], bw[cur][t], acc[mt][t]);
+        if (ks < 7) {
+          // next step's fragment reads first, then each MFMA followed by a
+          // share of the next step's dequantisation
+          __builtin_amdgcn_sched_group_barrier(0x100, MT, 0);
+#pragma unroll
+          for (int i = 0; i < MT * kLmNT; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, VPM, 0);
           }
         }
-    __syncthreads();
-    const int u = threadIdx.x & 31;
-#pragma unroll 4
-    for (int it = 0; it < BM / 8; ++it) {
-      const int R = it * 8 + (threadIdx.x >> 5);
-      const int out = s_out[R];
-      const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
-      const u32x4 v = *(const u32x4*)(row + ((u ^ (R & 15)) << 4));
-      if (out >= 0) *(u32x4*)(p.c + (size_t)out * p.N + nb * kLmBN + u * 8) = v;
+      }
+    };
+
+    // Issue order per step j: [wait, barrier] token rows of chunk j+1 (into
+    // the buffer chunk j-1 used), compute chunk j, weights of chunk j+2.
+    // Chunk j's token rows are therefore followed by exactly chunk j+1's
+    // weights (kLmBLoads loads) when step j waits for them.
+    BStage bs0, bs1;
+    load_b(bs0, chunk(0));
+    load_a(B0{}, chunk(0));
+    __builtin_amdgcn_sched_barrier(0);
+    load_b(bs1, chunk(1));
+    // step on chunk j: `cur` is j's buffer (0 or 1), the other gets chunk
+    // j+1. The last step waits for everything, since the count of loads
+    // issued after its token rows is not fixed there.
+    auto step = [&](int j, auto cur, BStage& b) {
+      if (j + 1 < n)
+        wait_vmcnt<kLmBLoads>();
+      else
+        wait_vmcnt<0>();
+      lds_barrier();
+      // (sched barriers keep the weight prefetch behind the token-row loads)
+      if constexpr (decltype(cur)::value == 0) {
+        load_a(B1{}, chunk(j + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(&s_a0[0], b);
+      } else {
+        load_a(B0{}, chunk(j + 1));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(&s_a1[0], b);
+      }
+      load_b(b, chunk(j + 2));
+    };
+    for (int j = 0;; j += 2) {
+      step(j, B0{}, bs0);
+      if (j + 1 >= n) break;
+      step(j + 1, B1{}, bs1);
+      if (j + 2 >= n) break;
     }
-  } else {
-    // fp32 partial sums: two passes of BM/2 rows of 256 columns (1 KiB)
+    wait_vmcnt<0>();
+
+    // Output. Accumulator element 4i + r of tile (mt, t) is token
+    // 32 mt + 8 i + 4 (l/32) + r, column 32 t + l % 32 of the wave's 64;
+    // direct stores would be 2-byte scatters. The tile goes through the two
+    // token buffers instead (free once every wave is past its last read),
+    // then out in full rows with 16-byte stores. Staged row R keeps its
+    // 16-byte unit u at u ^ (R % 16), so the accumulator-layout writes (rows
+    // 4 apart) and the row-major reads both fall in distinct banks.
+    __syncthreads();
+    if (p.split == 1) {
+      // bf16 tile: BMA rows of 256 columns (512 bytes), rows 0..63 in s_a0
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {
-      if (hp) __syncthreads();
-#pragma unroll
-      for (int mt = hp * kLmMT / 2; mt < (hp + 1) * kLmMT / 2; ++mt)
+      for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int L = mt * 32 + 8 * i + 4 * kq + r - hp * BM / 2;
-            uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
+            const int R = mt * 32 + 8 * i + 4 * kq + r;
+            const int out = s_out[R];
+            const float tw = (p.mode == 0 && p.topk_w && out >= 0) ? p.topk_w[out] : 1.0f;
+            uint8_t* row = mt < kLmMT / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
 #pragma unroll
             for (int t = 0; t < kLmNT; ++t) {
               const int C = w * 64 + t * 32 + l32;
-              *(float*)(row + (((C >> 2) ^ (L & 15)) << 4) + (C & 3) * 4) = acc[mt][t][4 * i + r];
+              *(uint16_t*)(row + (((C >> 3) ^ (R & 15)) << 4) + (C & 7) * 2) =
+                  (uint16_t)(cvt_pk_bf16(acc[mt][t][4 * i + r] * tw, 0.f) & 0xFFFFu);
             }
           }
       __syncthreads();
-      const int u = threadIdx.x & 63;
+      const int u = threadIdx.x & 31;
 #pragma unroll 4
-      for (int it = 0; it < BM / 8; ++it) {
-        const int L = it * 4 + (threadIdx.x >> 6);
-        const int out = s_out[hp * BM / 2 + L];
-        const uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
-        const u32x4 v = *(const u32x4*)(row + ((u ^ (L & 15)) << 4));
-        if (out >= 0)
-          *(u32x4*)(p.ws + ((size_t)sp * p.rows_cap + out) * p.N + nb * kLmBN + u * 4) = v;
+      for (int it = 0; it < BMA / 8; ++it) {
+        const int R = it * 8 + (threadIdx.x >> 5);
+        const int out = s_out[R];
+        const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+        const u32x4 v = *(const u32x4*)(row + ((u ^ (R & 15)) << 4));
+        if (out >= 0) *(u32x4*)(p.c + (size_t)out * p.N + nb * kLmBN + u * 8) = v;
+      }
+    } else {
+      // fp32 partial sums: passes of up to BM/2 rows of 256 columns (1 KiB)
+#pragma unroll
+      for (int hp = 0; hp < (BMA + BM / 2 - 1) / (BM / 2); ++hp) {
+        if (hp) __syncthreads();
+#pragma unroll
+        for (int mt = hp * kLmMT / 2; mt < min((hp + 1) * kLmMT / 2, MT); ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int L = mt * 32 + 8 * i + 4 * kq + r - hp * BM / 2;
+              uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
+#pragma unroll
+              for (int t = 0; t < kLmNT; ++t) {
+                const int C = w * 64 + t * 32 + l32;
+                *(float*)(row + (((C >> 2) ^ (L & 15)) << 4) + (C & 3) * 4) =
+                    acc[mt][t][4 * i + r];
+              }
+            }
+        __syncthreads();
+        const int u = threadIdx.x & 63;
+        constexpr int kPassRows = BM / 2;
+#pragma unroll 4
+        for (int it = 0; it < min(kPassRows, BMA - hp * kPassRows) / 4; ++it) {
+          const int L = it * 4 + (threadIdx.x >> 6);
+          const int out = s_out[hp * kPassRows + L];
+          const uint8_t* row = L < BM / 4 ? &s_a0[L * 1024] : &s_a1[(L - BM / 4) * 1024];
+          const u32x4 v = *(const u32x4*)(row + ((u ^ (L & 15)) << 4));
+          if (out >= 0)
+            *(u32x4*)(p.ws + ((size_t)sp * p.rows_cap + out) * p.N + nb * kLmBN + u * 4) = v;
+        }
       }
     }
+  };
+  switch (groups) {
+    case 0: break;   // no valid row: nothing to compute or store
+    case 1: body(std::integral_constant<int, 1>{}); break;
+    case 2: body(std::integral_constant<int, 2>{}); break;
+    case 3: body(std::integral_constant<int, 3>{}); break;
+    default: body(std::integral_constant<int, 4>{}); break;
   }
 }
 

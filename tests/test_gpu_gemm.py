@@ -235,10 +235,10 @@ def masked(a_bits, masked_m, expected_m, w, s, override=None):
 
 @pytest.mark.parametrize("integer", [False, True])
 def test_contiguous(gpu, integer):
-    E, K, N = 5, 512, 256
+    E, K, N = 8, 512, 256
     rng = np.random.default_rng(20 + integer)
-    wl = inputs.make_contiguous("c", 3, E, 0, K, N // 2, counts=[130, 0, 7, 128, 1],
-                                weights=False)
+    wl = inputs.make_contiguous("c", 3, E, 0, K, N // 2,
+                                counts=[130, 0, 7, 128, 1, 40, 70, 100], weights=False)
     m_idx = wl["m_indices"]
     w, s = weights(rng, E, N, K, integer)
     a = bf16_small_ints(rng, (m_idx.size, K)) if integer else wl["a"]
@@ -311,9 +311,11 @@ LARGE_SHAPES = [  # (E, T, topk, K, N): >= 80 rows per expert
 ]
 
 
-# expert row counts on both sides of the 64-row boundary of a 128-row tile:
-# tiles whose tokens all sit in rows 0..63 take the half-tile launch
-HALF_TILE_COUNTS = [1, 63, 64, 65, 127, 128, 129, 191, 192, 193, 0, 256]
+# expert row counts on both sides of every 32-row group boundary of a 128-row
+# tile: the large-M kernel computes only the groups that hold tokens, so a
+# tile ending an expert's rows runs with 1, 2, 3 or 4 groups
+HALF_TILE_COUNTS = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 191, 192, 193,
+                    0, 256, 287]
 
 
 @pytest.mark.parametrize("split", [1, 2])
@@ -332,9 +334,9 @@ def test_large_m_half_tiles_bitwise(gpu, split):
 
 @pytest.mark.parametrize("split", [1, 2])
 def test_large_m_masked_half_tiles_bitwise(gpu, split):
-    E, Mb, K, N = 6, 256, 256, 256
+    E, Mb, K, N = 11, 256, 256, 256
     rng = np.random.default_rng(80 + split)
-    masked_m = np.array([0, 1, 64, 65, 129, 256], np.int32)
+    masked_m = np.array([0, 1, 31, 33, 64, 65, 96, 97, 129, 161, 256], np.int32)
     w, s = weights(rng, E, N, K, integer=True)
     a = bf16_small_ints(rng, (E, Mb, K))
     large = {"kernel": qma.KERNEL_LARGE_M, "block_m": 128, "block_n": 256, "waves_k": 1,
