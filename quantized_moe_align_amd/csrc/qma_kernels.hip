@@ -462,31 +462,23 @@ __device__ __forceinline__ bool decode_bid(const GemmParams& p, int& tile, int& 
   return tile < p.num_tiles;
 }
 
-// Workgroup order of the large-M kernel. A token tile is read by every
-// column block, and a weight slice (256 columns of one expert) by every
-// token tile of the expert. The work items (token tile, column block,
-// split) are listed tile by tile (in groups of kLmGroup tiles sharing a
-// column block when that is > 1), and XCD x walks the x-th eighth of the
-// list in order: a tile's column blocks run together on one XCD, and so do
-// the same column block of an expert's consecutive tiles, so both stay in
-// that XCD's L2. The list covers only tiles that hold rows (the routed
-// count is read on the device), so every XCD gets an equal share of work.
-constexpr int kLmGroup = 1;
+// Workgroup order of the large-M kernel. Workgroup i runs on XCD i % 8.
+// The routed tiles are dealt to the XCDs in turn (XCD x takes tiles x,
+// x + 8, ...), each with all of its (column block, split) pieces, which run
+// together so that the tile's token rows stay in that XCD's L2. Dealing in
+// turn spreads a large expert's full tiles, and the partly filled tiles that
+// end each expert's rows, evenly over the XCDs; contiguous ranges of the
+// tile list would put a large expert's tiles on one or two XCDs, which then
+// set the launch time. The routed tile count is read on the device.
 __device__ __forceinline__ bool decode_bid_lm(const GemmParams& p, int& tile, int& nb, int& sp) {
   const int ntiles = p.mode == 0 ? min(*p.ntp / p.BM, p.num_tiles) : p.num_tiles;
   const int per = p.nblocks * p.split;
-  const int items = ntiles * per;
-  const int chunk = (items + 7) >> 3;
   const int bid = blockIdx.x;
   const int j = bid >> 3;
-  if (j >= chunk) return false;
-  const int i = (bid & 7) * chunk + j;
-  if (i >= items) return false;
-  const int s = i / (kLmGroup * per);
-  const int rem = i - s * kLmGroup * per;
-  const int g = min(kLmGroup, ntiles - s * kLmGroup);
-  const int nbsp = rem / g;
-  tile = s * kLmGroup + (rem - nbsp * g);
+  const int s = j / per;
+  tile = (bid & 7) + 8 * s;
+  if (tile >= ntiles) return false;
+  const int nbsp = j - s * per;
   nb = nbsp / p.split;
   sp = nbsp - nb * p.split;
   return true;
