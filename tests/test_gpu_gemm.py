@@ -332,6 +332,23 @@ def test_large_m_half_tiles_bitwise(gpu, split):
     assert np.array_equal(got, rne(ref))
 
 
+def test_large_m_several_rounds_per_xcd_bitwise(gpu):
+    # 45 tiles dealt to the 8 XCDs (5 or 6 each) x 16 column blocks: each
+    # XCD's list spans more than one round of its workgroup slots, and the
+    # ragged experts' last tiles are partly filled
+    K, N = 256, 4096
+    counts = [2200, 1300, 900, 700, 33, 3]
+    E = len(counts)
+    rng = np.random.default_rng(91)
+    w, s = weights(rng, E, N, K, integer=True)
+    ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts))[:, None]
+    a = bf16_small_ints(rng, (ids.shape[0], K))
+    got, plan = indexed(a, 1, ids, w, s, force_bm=128, override={"split_k": 1})
+    assert plan.kernel == qma.KERNEL_LARGE_M and plan.block_n == 256
+    ref = O.moe_gemm_by_slot(a, 1, ids, w, s)
+    assert np.array_equal(got, rne(ref))
+
+
 @pytest.mark.parametrize("split", [1, 2])
 def test_large_m_masked_half_tiles_bitwise(gpu, split):
     E, Mb, K, N = 11, 256, 256, 256
