@@ -145,7 +145,8 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->n_stream = 1;
   if (wk == 1 && split == 1 && tm == 1 && ntw >= 2 && L.k_chunks < qma::kStreamChunks) {
     const int32_t nblocks = L.N / p->block_n;
-    int32_t ns = std::min<int32_t>(ceil_div(qma::kStreamChunks, (int32_t)L.k_chunks), nblocks);
+    int32_t ns =
+        std::min<int32_t>(ceil_div(qma::kStreamTargetChunks, (int32_t)L.k_chunks), nblocks);
     while (ns > 1 && (int64_t)tiles_m * ceil_div(nblocks, ns) < 4 * qma::kNumCUs) --ns;
     p->n_stream = std::max<int32_t>(ns, 1);
   }

@@ -134,11 +134,22 @@ def test_split_k_gate_turns_on_only_when_underfilled():
 
 
 def test_stream_rule():
-    # TP8 down share: K = 256 is two chunks, so a workgroup streams 4 column
-    # blocks (8 chunks) and the grid keeps >= 4 workgroups per CU
+    # TP8 down share: K = 256 is two chunks, so a workgroup streams 7 column
+    # blocks (14 chunks) and the grid keeps >= 4 workgroups per CU
     d = _plan(384, 7168, 256, 256, 8)
     assert d.kernel == qma.KERNEL_SMALL_M and d.waves_k == 1 and d.split_k == 1
-    assert d.n_stream == 4
+    assert d.n_stream == 7
+    # fewer tiles: the stream shortens until the grid holds 4 workgroups per
+    # CU, and no further
+    for E, T in ((96, 64), (48, 32), (16, 16)):
+        p = _plan(E, 7168, 256, T, 8)
+        nb = 7168 // p.block_n
+        tiles_m = p.est_tiles // nb
+        ns = p.n_stream
+        wgs = lambda k: tiles_m * -(-nb // k)
+        assert 1 <= ns <= 7
+        assert ns == 1 or wgs(ns) >= 4 * 256
+        assert ns == 7 or wgs(ns + 1) < 4 * 256
     assert _plan(48, 7168, 2048, 558, 1).n_stream == 1      # EP8 down: K long enough
     assert _plan(48, 4096, 7168, 558, 1).n_stream == 1      # K split across waves
     assert _plan(8, 256, 128, 64, 2).n_stream == 1          # grid too small to stream
