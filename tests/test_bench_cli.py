@@ -42,3 +42,23 @@ def test_traffic_summaries_parse():
         assert d["workload"] in os.path.basename(f)
         assert d["bytes_per_launch"] > 0 and d["read_factor"] > 0 and d["write_factor"] > 0
         assert len(d["src_sha"]) == 16
+
+
+def test_algorithmic_work_per_expert_and_per_row():
+    # W4-g32 costs N*K*9/16 bytes of packed weights and scales per expert and
+    # GEMM; 2*N*K flops per routed row and GEMM. At the EP8 shapes (hidden
+    # 7168, intermediate 2048) that is 16,515,072 + 8,257,536 bytes per expert
+    # and 88,080,384 flops per row; at the TP8 share (intermediate 256)
+    # 2,064,384 + 1,032,192 bytes and 11,010,048 flops.
+    from quantized_moe_align_amd import inputs
+    bench = _bench()
+    for name, gu_e, dn_e, fl_row in (("ep8_decode", 16515072, 8257536, 88080384),
+                                     ("tp8", 2064384, 1032192, 11010048),
+                                     ("masked", 16515072, 8257536, 88080384)):
+        wl = inputs.make(name, seed=0, weights=False)
+        w = bench.algorithmic_work(wl)
+        K, I, ne, rows = wl.K, wl.I, w["experts_with_rows"], w["rows"]
+        a_rows = rows if name != "tp8" else wl.T
+        assert w["gate_up_bytes"] == ne * gu_e + a_rows * K * 2 + rows * 2 * I * 2, name
+        assert w["down_bytes"] == ne * dn_e + rows * I * 2 + rows * K * 2, name
+        assert w["gate_up_flops"] + w["down_flops"] == rows * fl_row, name
