@@ -572,3 +572,32 @@ def test_dynamic_schedule_grouped(gpu):
     row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
     assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N), row_e.reshape(-1),
                       "dynamic masked")
+
+
+# ---- degenerate routing: nothing to compute --------------------------------
+
+@pytest.mark.parametrize("force_bm", [16, 32, 64, 128])
+def test_indexed_no_routed_slot_writes_nothing(gpu, force_bm):
+    # every slot routed off this rank (-1): moe_align pads nothing, every
+    # GEMM workgroup exits, and the output keeps its pre-filled pattern
+    E, T, topk, K, N = 4, 40, 2, 256, 256
+    rng = np.random.default_rng(200 + force_bm)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = np.full((T, topk), -1, np.int32)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=force_bm)
+    assert plan.block_m == force_bm
+    assert np.all(got == SENT)
+
+
+def test_grouped_with_no_valid_rows_writes_nothing(gpu):
+    E, K, N = 3, 256, 256
+    rng = np.random.default_rng(210)
+    w, s = weights(rng, E, N, K)
+    m_idx = np.full(2 * 128, -1, np.int32)                 # two padding-only blocks
+    a = inputs.bf16_normal(rng, (m_idx.size, K))
+    for override in (None, {"kernel": 1, "block_m": 16, "block_n": 64, "waves_k": 4}):
+        assert np.all(contiguous(a, m_idx, w, s, override) == SENT)
+    a3 = inputs.bf16_normal(rng, (E, 64, K))
+    got = masked(a3, np.zeros(E, np.int32), 32, w, s)
+    assert np.all(got == SENT)
