@@ -357,6 +357,8 @@ def main():
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
         "kernel_us_mean": {k: round(v, 2) for k, v in us.items()},
         "kernel_us_median": {k: round(v, 2) for k, v in med.items()},
+        "kernel_us_p10_p90": {k: [round(float(np.percentile(v, 10)), 2),
+                                  round(float(np.percentile(v, 90)), 2)] for k, v in ev.items()},
         "gemm_pair_effective": {"GB/s": round(total_bytes / ((us["gate_up"] + us["down"]) * 1e-6)
                                               / 1e9, 1),
                                 "TFLOP/s": round(total_flops / ((us["gate_up"] + us["down"])
