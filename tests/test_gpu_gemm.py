@@ -79,7 +79,7 @@ def test_indexed_random_within_tolerance(gpu, shape, force_bm):
     assert_per_expert(got, ref, slot_experts(ids, E), f"{shape} bm={plan.block_m}")
 
 
-KERNEL_INSTANCES = [(0, 0, 0), (16, 1, 4), (16, 2, 1), (16, 4, 2), (16, 4, 4), (16, 4, 1),
+KERNEL_INSTANCES = [(0, 0, 0), (16, 1, 4), (16, 1, 1), (16, 2, 1), (16, 4, 2), (16, 4, 4), (16, 4, 1),
                     (32, 4, 4), (32, 2, 2), (32, 1, 1), (32, 4, 1), (32, 2, 1), (64, 2, 4),
                     (64, 1, 2)]                       # (force_bm, ntw, waves_k); 0 = planner
 
