@@ -465,6 +465,41 @@ def test_graph_capture_replays_match_eager(gpu):
         assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
 
 
+def test_graph_capture_large_m_split_k(gpu):
+    # the large-M kernel with split-K (fp32 partials in the workspace, then
+    # the reduce kernel) for both projections, captured and replayed
+    E, T, K, I = 3, 300, 512, 256
+    rng = np.random.default_rng(77)
+    w13, s13 = weights(rng, E, 2 * I, K)
+    w2, s2 = weights(rng, E, K, I)
+    moe = IndexedMoE(ExpertWeights(w13, s13), ExpertWeights(w2, s2), T, 1, force_block_m=128)
+    assert moe.plan13.kernel == qma.KERNEL_LARGE_M and moe.plan2.kernel == qma.KERNEL_LARGE_M
+    moe.plan13.split_k = 2
+    moe.plan2.split_k = 2
+    moe.ws13 = workspace_for(moe.plan13)
+    moe.ws2 = workspace_for(moe.plan2)
+    a = to_device(inputs.bf16_normal(rng, (T, K)))
+    ids = to_device(rng.integers(0, E, (T, 1)).astype(np.int32))
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        moe.forward(a, ids)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    eager = to_host(moe.c2, bf16=True).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(a, ids)
+    for i in range(3):
+        moe.c2.fill_(0)
+        moe.c1.fill_(0)
+        moe.ws13.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
+
+
 # Streaming small-M (one workgroup walks several column blocks of its
 # expert): (E, T, topk, K, N, block_n, n_stream). 7 or 14 column blocks, so
 # some streams end on a partial group.
