@@ -500,6 +500,71 @@ def test_graph_capture_large_m_split_k(gpu):
         assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
 
 
+@pytest.mark.parametrize("kind", ["contiguous", "masked", "masked_dynamic"])
+def test_graph_capture_grouped(gpu, kind):
+    # grouped paths captured and replayed; the masked replay after new
+    # device-side row counts must match an eager run with those counts
+    from quantized_moe_align_amd.moe import GroupedMoE
+    E, K, I = 4, 256, 128
+    rng = np.random.default_rng(88)
+    path = qma.PATH_GROUPED_CONTIGUOUS if kind == "contiguous" else qma.PATH_GROUPED_MASKED
+    w13, s13 = weights(rng, E, 2 * I, K)
+    w2, s2 = weights(rng, E, K, I)
+    W13, W2 = ExpertWeights(w13, s13, path), ExpertWeights(w2, s2, path)
+    if kind == "contiguous":
+        m_idx = np.repeat(np.arange(E, dtype=np.int32), 128)
+        m_idx[100:128] = -1
+        moe = GroupedMoE(W13, W2, m_idx.size)
+        a = to_device(inputs.bf16_normal(rng, (m_idx.size, K)))
+        index = to_device(m_idx)
+        counts2 = None
+    else:
+        moe = GroupedMoE(W13, W2, 64, 32)
+        if kind == "masked_dynamic":
+            assert moe.set_schedule(qma.SCHEDULE_DYNAMIC) == (True, True)
+        a = to_device(inputs.bf16_normal(rng, (E, 64, K)))
+        index = to_device(np.array([32, 7, 0, 64], np.int32))
+        counts2 = np.array([5, 64, 33, 0], np.int32)
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(st):
+        moe.forward(a, index)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    eager = to_host(moe.c2, bf16=True).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(a, index)
+    for i in range(3):
+        moe.c2.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(moe.c2, bf16=True)
+        if counts2 is None:                     # padding rows are never written
+            valid = m_idx >= 0
+            assert np.array_equal(got[valid], eager[valid]), f"replay {i}"
+        else:
+            rows = to_host(index)
+            for e in range(E):
+                assert np.array_equal(got.reshape(E, 64, K)[e, :rows[e]],
+                                      eager.reshape(E, 64, K)[e, :rows[e]]), (i, e)
+    if counts2 is not None:
+        index.copy_(torch.from_numpy(counts2))
+        moe.c2.fill_(0)
+        moe.forward(a, index)
+        torch.cuda.synchronize()
+        eager2 = to_host(moe.c2, bf16=True).copy()
+        moe.c2.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        got = to_host(moe.c2, bf16=True).reshape(E, 64, K)
+        for e in range(E):
+            assert np.array_equal(got[e, :counts2[e]],
+                                  eager2.reshape(E, 64, K)[e, :counts2[e]]), e
+
+
 # Streaming small-M (one workgroup walks several column blocks of its
 # expert): (E, T, topk, K, N, block_n, n_stream). 7 or 14 column blocks, so
 # some streams end on a partial group.
