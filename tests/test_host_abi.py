@@ -4,10 +4,14 @@ rules. No call here reaches a kernel launch."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
 from quantized_moe_align_amd import qma
+
+ROOT_DIR = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
                       "include", "qma.h")
@@ -265,3 +269,19 @@ def test_host_checks_before_any_launch(L):
     finally:
         qma.qma_layer_destroy(lay)
         qma.qma_layer_destroy(other)
+
+
+def test_missing_library_fails_loudly():
+    # no CPU fallback: without the built HIP library every entry point raises
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from quantized_moe_align_amd import qma\n"
+        "qma.LIB_PATH = '/nonexistent/libqma.so'\n"
+        "try:\n"
+        "    qma.qma_layer_create(8, 256, 256)\n"
+        "except ImportError as e:\n"
+        "    print('raised', e)\n"
+        "else:\n"
+        "    print('no error')\n" % ROOT_DIR)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
+    assert "raised" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
