@@ -91,6 +91,16 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     if (ntw > 1 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
         L.N % (64 * (ntw / 2)) == 0)
       ntw /= 2;
+    // 16-row tiles with long K and wide N (>= 8 blocks of 256) take 256
+    // columns when that still fills a whole round of three workgroups per CU
+    // (the EP8 gate_up share: 48 tiles x 16 blocks = 768 workgroups;
+    // measured 134.4 vs 136.9 us against 128 columns). With fewer tiles (the
+    // EP16 share: 384 workgroups) the wide block leaves half the slots empty
+    // and was 27 % slower; on the narrow TP8 gate_up share (N = 512, 2
+    // blocks per tile) it was 1 % slower.
+    if (tm == 1 && ntw == 2 && L.k_chunks >= 4 * qma::kStreamChunks && L.N % 256 == 0 &&
+        L.N / 256 >= 8 && (int64_t)tiles_m * (L.N / 256) >= 3 * qma::kNumCUs)
+      ntw = 4;
     // Between one and two workgroups per CU with long K (an EP32 gate_up
     // share: 384 tiles), two wave pairs splitting K keep more weight loads in
     // flight per workgroup than four waves side by side (measured 52 vs

@@ -92,8 +92,12 @@ def _plan(E, N, K, T, topk, force=0):
 def test_plan_decode_ep8():
     p = _plan(48, 4096, 7168, 576, 1)
     assert p.kernel == qma.KERNEL_SMALL_M and p.block_m == 16
-    assert p.block_n == 128 and p.waves_k == 1 and p.split_k == 1  # 48 x 32 tiles
+    # 48 tiles x 16 blocks of 256 columns: one full round of three per CU
+    assert p.block_n == 256 and p.waves_k == 1 and p.split_k == 1
     assert p.k_depth == 256                            # shared-row kernel: 2 chunks
+    # EP16 share: at 256 columns only 384 workgroups, so 128 columns
+    q = _plan(24, 4096, 7168, 288, 1)
+    assert q.block_m == 16 and q.block_n == 128 and q.waves_k == 1
     assert p.tok_e_x100 == 1200 and p.rows == 576
     assert qma.qma_workspace_bytes(p) == 0
 
