@@ -114,9 +114,12 @@ def cpu_baseline(wl, budget_s):
     from oracle import qma_oracle as O
     try:
         from threadpoolctl import threadpool_info
-        threads = max([t.get("num_threads", 1) for t in threadpool_info()] + [1])
+        pools = threadpool_info()
+        threads = max([t.get("num_threads", 1) for t in pools] + [1])
+        blas = ", ".join(sorted({f"{t.get('internal_api')} {t.get('version')}" for t in pools
+                                 if t.get("user_api") == "blas"})) or "unknown"
     except Exception:                                     # pragma: no cover
-        threads = 1
+        threads, blas = 1, "unknown"
     E, K, I = wl.E, wl.K, wl.I
     if wl.kind == "indexed":
         se = np.where((wl["topk_ids"] >= 0) & (wl["topk_ids"] < E), wl["topk_ids"], -1)
@@ -151,7 +154,17 @@ def cpu_baseline(wl, budget_s):
         experts.append(e)
         if t_total >= budget_s:
             break
-    return t_total, done_bytes, done_flops, threads, experts
+    return t_total, done_bytes, done_flops, threads, experts, blas
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:                                       # pragma: no cover
+        pass
+    return "unknown"
 
 
 def practical_roofs(torch, dev):
@@ -335,9 +348,10 @@ def main():
 
     cpu = None
     if args.cpu_budget > 0:
-        t_cpu, b_cpu, f_cpu, threads, experts = cpu_baseline(wl, args.cpu_budget)
+        t_cpu, b_cpu, f_cpu, threads, experts, blas = cpu_baseline(wl, args.cpu_budget)
         cpu = {"value": round((b_cpu / t_cpu / 1e9) if hbm else (f_cpu / t_cpu / 1e12), 4),
                "unit": unit, "cores": threads, "kind": "oracle",
+               "host": {"cpu": host_cpu_model(), "nproc": os.cpu_count(), "blas": blas},
                "sample": f"experts {experts[0]}..{experts[-1]} ({len(experts)} of "
                          f"{work['experts_with_rows']}) of the same workload: gate_up, "
                          f"activation and down per expert in float64, {t_cpu:.1f} s"}
