@@ -169,10 +169,12 @@ def host_cpu_model():
 
 def practical_roofs(torch, dev):
     """What plain reference work reaches on this GPU, next to the vendor
-    peaks: a 1 GiB device copy (torch's copy kernel; read + write bytes) and a
-    dense 8192^3 bf16 matmul (the vendor GEMM library through torch). Both are
-    measured after the timed region, back to back with a settle, and serve as
-    context only; neither is on the product path."""
+    peaks: a 1 GiB device copy (torch's copy kernel; read + write bytes), a
+    16-row bf16 product against a 1 GiB bf16 weight matrix (weight read
+    bytes; the decode-shaped read roof) and a dense 8192^3 bf16 matmul, the
+    last two through the vendor GEMM library via torch. All are measured
+    after the timed region, back to back with a settle, and serve as context
+    only; none is on the product path."""
     import time as _t
 
     def run(fn, n):
@@ -197,14 +199,23 @@ def practical_roofs(torch, dev):
     dst = torch.empty_like(src)
     t_copy = run(lambda: dst.copy_(src), 20)
     del src, dst
+    # read-bound: 16 bf16 token rows against a 1 GiB bf16 weight matrix
+    # (the vendor GEMM library's skinny product reads the matrix once)
+    kk, nn = 16384, 32768
+    wg = torch.empty(nn, kk, dtype=torch.bfloat16, device=dev).fill_(0.5)
+    xg = torch.randn(16, kk, device=dev).to(torch.bfloat16)
+    t_read = run(lambda: torch.nn.functional.linear(xg, wg), 20)
+    del wg, xg
     n = 8192
     a = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
     b = torch.randn(n, n, device=dev).to(torch.bfloat16).contiguous()
     t_mm = run(lambda: torch.mm(a, b), 10)
     del a, b
     return {"copy_GBps": round(2 * nbytes / t_copy / 1e9, 1),
+            "gemv16_read_GBps": round(kk * nn * 2 / t_read / 1e9, 1),
             "dense_bf16_gemm_TFLOPs": round(2 * n ** 3 / t_mm / 1e12, 1),
-            "note": "1 GiB device copy (read + write); dense 8192^3 bf16 matmul via torch"}
+            "note": "1 GiB device copy (read + write); 16 bf16 rows x 1 GiB bf16 weights "
+                    "(weight reads); dense 8192^3 bf16 matmul; all via torch"}
 
 
 def main():
