@@ -289,3 +289,37 @@ def test_missing_library_fails_loudly():
         "    print('no error')\n" % ROOT_DIR)
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=120)
     assert "raised" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
+
+
+def test_planner_invariants_over_shapes():
+    # every plan the planner returns names an existing kernel instance and
+    # follows the documented rules, over a grid of layer and batch shapes
+    import itertools
+    for E, N, K, T, topk in itertools.product((1, 8, 48, 384), (256, 512, 4096, 7168),
+                                              (256, 2048, 7168), (1, 17, 256, 8192), (1, 8)):
+        lay = qma.qma_layer_create(E, N, K)
+        try:
+            p = qma.qma_plan_indexed(lay, T, topk, 0)
+        finally:
+            qma.qma_layer_destroy(lay)
+        shape = (E, N, K, T, topk)
+        assert N % p.block_n == 0, shape
+        assert 1 <= p.split_k <= 8 and p.waves_k in (1, 2, 4) and p.n_stream >= 1, shape
+        if p.kernel == qma.KERNEL_LARGE_M:
+            assert p.block_m == 128 and p.block_n == 256 and N % 256 == 0, shape
+            assert T * topk / E >= 80, shape
+        else:
+            assert p.kernel == qma.KERNEL_SMALL_M and p.block_m in (16, 32, 64), shape
+            tm, ntw = p.block_m // 16, p.block_n // (16 * (4 // p.waves_k))
+            assert tm * ntw <= 8 and ntw in (1, 2, 4), shape
+            if p.n_stream > 1:                               # streaming: short K only
+                assert K // 128 < 8 and p.block_m == 16 and p.split_k == 1, shape
+        if p.split_k > 1:
+            # split-K only when the grid underfills the CUs, and never below
+            # two 128-wide K chunks per wave (four per split for large-M)
+            assert p.est_tiles < 256, shape
+            per_split = 4 if p.kernel == qma.KERNEL_LARGE_M else 2 * p.waves_k
+            assert K // 128 >= per_split * p.split_k, shape
+            assert qma.qma_workspace_bytes(p) > 0, shape
+        else:
+            assert qma.qma_workspace_bytes(p) == 0, shape
