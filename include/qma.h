@@ -106,8 +106,10 @@ typedef enum qma_kernel {
  * QMA_ERR_INVALID_ARG and before any launch, a plan made for another layer
  * or one that names no compiled kernel instance (small-M: block_m in
  * {16, 32, 64}, waves_k in {1, 2, 4}, at most 8 16x16 tiles per wave;
- * large-M: a 128 x 256 block). k_depth outside an instance's supported
- * depths falls back to that instance's default. */
+ * large-M: a 128 x 256 block), or whose split_k is outside [1, 8] or above
+ * K/128 (every K partition owns at least one 128-wide chunk). k_depth
+ * outside an instance's supported depths falls back to that instance's
+ * default. */
 typedef struct qma_plan {
   int32_t path;          /* qma_path of the layer */
   int32_t kernel;        /* qma_kernel */
@@ -153,8 +155,10 @@ typedef enum {
  * integration sections). N is the output width, K the reduction length.
  * Errors: any scheme other than the accepted one -> QMA_ERR_UNSUPPORTED;
  * E < 1, N % 16 != 0, K % 128 != 0, N or K < 1, a null pointer ->
- * QMA_ERR_INVALID_ARG. The caller owns *out and frees it with
- * qma_layer_destroy. */
+ * QMA_ERR_INVALID_ARG. K must be a multiple of 128, not only of the scale
+ * group (32): the packed layout is built from 128-wide K chunks, and every
+ * projection of the pages' models has such a K (7168, 2048, 256). The
+ * caller owns *out and frees it with qma_layer_destroy. */
 qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
                             int32_t K, qma_path path, qma_layer_t** out);
 void qma_layer_destroy(qma_layer_t* layer);
@@ -246,10 +250,14 @@ qma_status qma_moe_align(const int32_t* topk_ids, int32_t T, int32_t topk,
 
 /* Routing validation, the opt-in check the trusted path skips ([release]
  * runtime considerations). Reads the buffers back: it SYNCHRONISES the
- * stream and is not capturable. It checks that the buffers are exactly
- * what qma_moe_align defines for topk_ids, and that every id is in
- * [-1, E). It returns QMA_ERR_ROUTING on the first violation, with detail
- * text. */
+ * stream and is not capturable. It checks that every id is in [-1, E),
+ * recomputes on the host the buffers qma_moe_align defines for topk_ids,
+ * and compares all of them over the whole capacity: num_tokens_padded,
+ * sorted_ids [sorted_cap] (slot order inside each segment, the sentinel in
+ * every padding position and in the tail) and expert_ids
+ * [ceil(sorted_cap/block_m)] (routed blocks and the -1 tail). It returns
+ * QMA_ERR_ROUTING on the first difference, with text naming the position.
+ * Errors: negative sizes or a null buffer -> QMA_ERR_INVALID_ARG. */
 qma_status qma_validate_routing(const int32_t* topk_ids, int32_t T,
                                 int32_t topk, int32_t E, int32_t block_m,
                                 const int32_t* sorted_ids,
@@ -281,8 +289,8 @@ qma_status qma_validate_contiguous(const int32_t* m_indices, int32_t M,
  *   c        [num_slots, N] bf16; rows no block names are left untouched
  *   ws       qma_workspace_bytes(plan) bytes of device memory, or NULL if 0
  * Errors: a plan made for another layer shape or path, a null pointer, or
- * a sorted_cap below the bound -> QMA_ERR_INVALID_ARG; a short workspace
- * -> QMA_ERR_WORKSPACE. */
+ * a sorted_cap below num_slots + E*(block_m - 1) (the qma_align_sizes
+ * bound) -> QMA_ERR_INVALID_ARG; a short workspace -> QMA_ERR_WORKSPACE. */
 qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
                             const uint16_t* a, int32_t a_rows,
                             int32_t a_row_div, const void* packed_w,

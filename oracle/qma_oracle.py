@@ -37,8 +37,7 @@ GROUP = 32
 
 # --------------------------------------------------------------------------
 # bf16 <-> float64  (BF16 activations and scales: [release] TL;DR;
-# [announce] integration section, "schema supports uint4, group-32, BF16
-# scales")
+# [announce] integration section: uint4 weights with group-32 BF16 scales)
 # --------------------------------------------------------------------------
 
 def bf16_to_f64(bits: np.ndarray) -> np.ndarray:

@@ -236,6 +236,10 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);
   if (plan->split_k < 1 || plan->split_k > 8)
     return fail(QMA_ERR_INVALID_ARG, "plan has bad split_k %d", plan->split_k);
+  // every K partition must own at least one 128-wide chunk
+  if (plan->split_k > L.k_chunks)
+    return fail(QMA_ERR_INVALID_ARG, "split_k %d exceeds the %lld K chunks of 128", plan->split_k,
+                (long long)L.k_chunks);
   if (plan->schedule != QMA_SCHEDULE_SEMI_STATIC &&
       (plan->schedule != QMA_SCHEDULE_DYNAMIC || plan->kernel != QMA_KERNEL_SMALL_M ||
        plan->waves_k != 1 || plan->split_k != 1 || plan->n_stream != 1 ||
@@ -515,27 +519,43 @@ qma_status qma_validate_routing(const int32_t* topk_ids, int32_t T, int32_t topk
   for (int64_t i = 0; i < R; ++i)
     if (ids[i] < -1 || ids[i] >= E)
       return fail(QMA_ERR_ROUTING, "topk_ids[%lld] = %d outside [-1, %d)", (long long)i, ids[i], E);
-  const int64_t n = ntp[0];
-  if (n < 0 || n > sorted_cap || n % block_m != 0)
-    return fail(QMA_ERR_ROUTING, "num_tokens_padded %lld invalid (cap %d, block %d)",
-                (long long)n, sorted_cap, block_m);
-  std::vector<int32_t> seen((size_t)R, 0);
-  for (int64_t p = 0; p < n; ++p) {
-    const int32_t e = experts[p / block_m];
-    if (e < 0 || e >= E)
-      return fail(QMA_ERR_ROUTING, "expert_ids[%lld] = %d outside [0, %d)", (long long)(p / block_m), e, E);
-    const int32_t sl = sorted[p];
-    if (sl < 0) return fail(QMA_ERR_ROUTING, "sorted_ids[%lld] = %d negative", (long long)p, sl);
-    if (sl >= R) continue;  // padding
-    if (ids[sl] != e)
-      return fail(QMA_ERR_ROUTING, "sorted_ids[%lld] = slot %d of expert %d placed in a block of expert %d",
-                  (long long)p, sl, ids[sl], e);
-    if (seen[sl]++)
-      return fail(QMA_ERR_ROUTING, "slot %d appears twice", sl);
-  }
+  // The buffers moe_align defines for these ids, recomputed on the host: a
+  // stable counting sort of the slots by expert, each expert padded with the
+  // sentinel R to a multiple of block_m, then the tails.
+  std::vector<int64_t> count((size_t)E, 0), start((size_t)E + 1, 0);
   for (int64_t i = 0; i < R; ++i)
-    if (ids[i] >= 0 && !seen[i])
-      return fail(QMA_ERR_ROUTING, "slot %lld (expert %d) is missing", (long long)i, ids[i]);
+    if (ids[i] >= 0) ++count[(size_t)ids[i]];
+  for (int32_t e = 0; e < E; ++e)
+    start[(size_t)e + 1] = start[(size_t)e] + (count[(size_t)e] + block_m - 1) / block_m * block_m;
+  const int64_t want_ntp = start[(size_t)E];
+  if (want_ntp > sorted_cap)
+    return fail(QMA_ERR_ROUTING, "sorted_cap %d is below the padded length %lld", sorted_cap,
+                (long long)want_ntp);
+  if (ntp[0] != want_ntp)
+    return fail(QMA_ERR_ROUTING, "num_tokens_padded %d, expected %lld", ntp[0],
+                (long long)want_ntp);
+  std::vector<int32_t> want_sorted((size_t)sorted_cap, (int32_t)R);
+  std::vector<int64_t> next(start.begin(), start.end() - 1);
+  for (int64_t i = 0; i < R; ++i)
+    if (ids[i] >= 0) want_sorted[(size_t)next[(size_t)ids[i]]++] = (int32_t)i;
+  std::vector<int32_t> want_experts((size_t)blocks, -1);
+  for (int32_t e = 0; e < E; ++e)
+    for (int64_t b = start[(size_t)e] / block_m; b < start[(size_t)e + 1] / block_m; ++b)
+      want_experts[(size_t)b] = e;
+  for (int64_t p = 0; p < sorted_cap; ++p) {
+    if (sorted[(size_t)p] == want_sorted[(size_t)p]) continue;
+    const char* where = p >= want_ntp ? "tail past num_tokens_padded"
+                        : want_sorted[(size_t)p] == R ? "expert padding"
+                                                      : "an expert's slot list";
+    return fail(QMA_ERR_ROUTING, "sorted_ids[%lld] = %d, expected %d (%s)", (long long)p,
+                sorted[(size_t)p], want_sorted[(size_t)p], where);
+  }
+  for (int64_t b = 0; b < blocks; ++b) {
+    if (experts[(size_t)b] == want_experts[(size_t)b]) continue;
+    return fail(QMA_ERR_ROUTING, "expert_ids[%lld] = %d, expected %d (%s)", (long long)b,
+                experts[(size_t)b], want_experts[(size_t)b],
+                b * block_m >= want_ntp ? "tail" : "routed block");
+  }
   return ok();
 }
 
@@ -574,6 +594,12 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
   if ((int64_t)a_rows * a_row_div < num_slots)
     return fail(QMA_ERR_INVALID_ARG, "a has %d rows; %d slots / %d need more", a_rows,
                 num_slots, a_row_div);
+  // The grid covers ceil(sorted_cap / block_m) blocks; below the moe_align
+  // bound, routed blocks past it would be skipped with no error.
+  const int64_t cap_bound = (int64_t)num_slots + (int64_t)layer->L.E * (plan->block_m - 1);
+  if (sorted_cap < cap_bound)
+    return fail(QMA_ERR_INVALID_ARG, "sorted_cap %d below the bound %lld (num_slots + E*(block_m-1))",
+                sorted_cap, (long long)cap_bound);
   if (!a || !packed_w || !sorted_ids || !expert_ids || !num_tokens_padded || !c)
     return fail(QMA_ERR_INVALID_ARG, "null buffer");
   if (!aligned(a, 16) || !aligned(c, 16) || !aligned(packed_w, 256))
@@ -582,7 +608,7 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
   if ((s = check_a_bytes(a_rows, layer->L.K)) != QMA_OK) return s;
   if ((s = check_grid(((int64_t)sorted_cap + plan->block_m - 1) / plan->block_m, plan)) != QMA_OK)
     return s;
-  if (sorted_cap == 0 || num_slots == 0) return ok();
+  if (num_slots == 0) return ok();
   qma::GemmArgs g{};
   g.layer = &layer->L;
   g.plan = plan;

@@ -1309,6 +1309,9 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
     // the buffer chunk j-1 used), compute chunk j, weights of chunk j+2.
     // Chunk j's token rows are therefore followed by exactly chunk j+1's
     // weights (kLmBLoads loads) when step j waits for them.
+    // A split that owns no K chunk (never planned; rejected on the host)
+    // keeps its zero accumulators and stores zero partial sums.
+    if (n > 0) {
     BStage bs0, bs1;
     load_b(bs0, chunk(0));
     load_a(B0{}, chunk(0));
@@ -1342,6 +1345,7 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
       if (j + 2 >= n) break;
     }
     wait_vmcnt<0>();
+    }
 
     // Output. Accumulator element 4i + r of tile (mt, t) is token
     // 32 mt + 8 i + 4 (l/32) + r, column 32 t + l % 32 of the wave's 64;

@@ -2,14 +2,20 @@
 
 This module is shared by the HIP path's callers (tests, bench) and by the
 oracle's callers. It produces raw bit patterns only -- bf16 as uint16, packed
-uint4 as int32 words, routing as int32 -- and holds none of the method's
-arithmetic: no unpacking, dequantisation, sorting, GEMM or activation.
+uint4 as int32 words, routing as int32 -- and holds none of the GEMM path's
+arithmetic: no unpacking, dequantisation, routing alignment, GEMM or
+activation. The one computation beyond sampling is on the input side: the
+router-routed workloads (tiny, tp8) pick each token's experts as the top-k of
+seeded N(0,1) logits, standing in for the router upstream of the path. That
+choice orders logits the way the library's router kernel does (descending,
+lower expert index on ties), but the kernel is checked against the oracle's
+router, never against this generator.
 
 Every tensor of a workload draws from its own child of one
 ``numpy.random.SeedSequence`` (PCG64), keyed by the tensor's name, so adding or
 changing one tensor never shifts the bits of another. Both sides of a parity
-check consume the same bits ("same routing sample": Chord blog, per-layer
-measurement section, on page 4).
+check consume the same bits, as the [announce] page's per-layer measurement
+section has both kernels run on the same routing sample.
 
 Workloads (shapes of one EP8 or TP8 rank's share of a Kimi K2.x MoE layer:
 hidden 7168, intermediate 2048, 384 experts, top-8):
@@ -24,7 +30,11 @@ hidden 7168, intermediate 2048, 384 experts, top-8):
 * ``contiguous``  48 experts x 128 rows, grouped_contiguous layout.
 * ``masked``      48 experts, 64-row budget, 32 valid rows each.
 * ``ep16_decode`` 24 local experts, counts U{9..15} (EP16 rank share).
-* ``ep32_decode`` 12 local experts, counts U{9..15} (split-K gate probe).
+* ``ep32_decode`` 12 local experts, counts U{9..15} (EP32 rank share).
+* ``ep8_mid``     48 local experts, counts U{40..56}: the 33..79 rows per
+                  expert between decode and the large-M threshold.
+* ``ep128_decode`` 3 local experts, counts U{9..15} (an EP128 rank share:
+                  so few tiles that the split-K gate turns on).
 """
 from __future__ import annotations
 
@@ -86,15 +96,14 @@ class Workload:
 
 
 def _router_topk(rng: np.random.Generator, T: int, E: int, topk: int):
-    """Softmax router over N(0,1) logits; top-k by descending probability.
-
-    Ties go to the lower expert index (stable sort); weights are the softmax
-    probabilities of the chosen experts, not renormalised.
-    """
+    """Routing input for router-routed workloads: each token's experts are
+    the top-k of seeded N(0,1) logits, by descending logit with ties to the
+    lower expert index (a stable sort); the weights are the softmax
+    probabilities of the chosen experts over all E, not renormalised."""
     logits = rng.standard_normal(size=(T, E), dtype=np.float32).astype(np.float64)
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :topk]
     z = np.exp(logits - logits.max(axis=1, keepdims=True))
     p = z / z.sum(axis=1, keepdims=True)
-    order = np.argsort(-p, axis=1, kind="stable")[:, :topk]
     w = np.take_along_axis(p, order, axis=1).astype(np.float32)
     return order.astype(np.int32), w
 
@@ -214,7 +223,8 @@ def make_masked(name, seed, E, budget, valid, K, I, expected_m=None,
 
 
 WORKLOADS = ("tiny", "ep8_decode", "tp8", "ep8_prefill", "ep8_prefill_span",
-             "contiguous", "masked", "ep16_decode", "ep32_decode")
+             "contiguous", "masked", "ep16_decode", "ep32_decode", "ep8_mid",
+             "ep128_decode")
 
 
 def make(name: str, seed: int = 0, weights: bool = True,
@@ -235,6 +245,12 @@ def make(name: str, seed: int = 0, weights: bool = True,
                                    weights, {"routing": "U{9..15} per expert"})
     if name == "ep32_decode":
         return make_count_workload(name, seed, uniform_counts(seed, 12), K, I,
+                                   weights, {"routing": "U{9..15} per expert"})
+    if name == "ep8_mid":
+        return make_count_workload(name, seed, uniform_counts(seed, 48, 40, 56), K, I,
+                                   weights, {"routing": "U{40..56} per expert"})
+    if name == "ep128_decode":
+        return make_count_workload(name, seed, uniform_counts(seed, 3), K, I,
                                    weights, {"routing": "U{9..15} per expert"})
     if name == "tp8":
         return make_router_workload(name, seed, 384, 256, 8, K,

@@ -70,35 +70,63 @@ def test_edge_cases(gpu):
 
 
 def test_validator_rejects_corruptions(gpu):
+    # the validator recomputes the buffers moe_align defines and compares all
+    # three over the whole capacity, so every class of corruption is caught:
+    # each one below still passes a check of slot membership alone
     wl = inputs.make("tiny", seed=5, weights=False)
     ids = wl["topk_ids"]
-    d_ids, s, e, n, cap = check(ids, wl.E, 16)
+    B = 16
+    d_ids, s, e, n, cap = check(ids, wl.E, B, extra=2 * B + 3)
     T, topk = ids.shape
+    R = T * topk
+    ntp = int(n.item())
 
-    def expect_bad(s2=None, e2=None, n2=None, ids2=None):
+    def expect_bad(s2=None, e2=None, n2=None, ids2=None, what=""):
         with pytest.raises(qma.QmaError) as ei:
-            qma.qma_validate_routing(d_ids if ids2 is None else ids2, T, topk, wl.E, 16,
+            qma.qma_validate_routing(d_ids if ids2 is None else ids2, T, topk, wl.E, B,
                                      s if s2 is None else s2, e if e2 is None else e2,
                                      n if n2 is None else n2, cap)
-        assert ei.value.status == qma.QMA_ERR_ROUTING
+        assert ei.value.status == qma.QMA_ERR_ROUTING, what
         return ei.value.detail
 
     sh = s.cpu().numpy()
-    R = T * topk
-    p = next(i for i in range(16, int(n.item())) if sh[i] < R)  # a slot of a later block
-    s2 = s.clone(); s2[0] = int(sh[p])                           # wrong block and twice
-    d = expect_bad(s2=s2)
-    assert "placed" in d or "twice" in d
-    s3 = s.clone(); s3[1] = s3[0]                                # duplicate
-    expect_bad(s2=s3)
-    e2 = e.clone(); e2[0] = wl.E                                 # expert out of range
-    expect_bad(e2=e2)
-    n2 = n.clone(); n2[0] = n[0] + 1                             # not a block multiple
-    expect_bad(n2=n2)
-    n3 = n.clone(); n3[0] = n[0] - 16                            # drops a block
-    expect_bad(n2=n3)
-    ids2 = d_ids.clone(); ids2[0, 0] = wl.E + 3                  # id outside [-1, E)
-    expect_bad(ids2=ids2)
+    eh = e.cpu().numpy()
+    # a slot placed in another expert's block (and listed twice)
+    p = next(i for i in range(B, ntp) if sh[i] < R and eh[i // B] != eh[0])
+    s2 = s.clone(); s2[0] = int(sh[p])
+    assert "sorted_ids[0]" in expect_bad(s2=s2, what="wrong block")
+    # two slots swapped inside one expert's segment (membership unchanged)
+    seg = next(i for i in range(ntp - 1) if sh[i] < R and sh[i + 1] < R and
+               eh[i // B] == eh[(i + 1) // B])
+    s3 = s.clone(); s3[seg], s3[seg + 1] = int(sh[seg + 1]), int(sh[seg])
+    assert "slot list" in expect_bad(s2=s3, what="swap inside a segment")
+    # a padding position holding another value >= R instead of the sentinel
+    pad = next(i for i in range(ntp) if sh[i] == R)
+    s4 = s.clone(); s4[pad] = R + 7
+    assert "padding" in expect_bad(s2=s4, what="wrong sentinel")
+    # junk in the sorted_ids tail past num_tokens_padded
+    s5 = s.clone(); s5[cap - 1] = 0
+    assert "tail" in expect_bad(s2=s5, what="junk tail")
+    # expert_ids: out of range in a routed block, and a junk tail entry
+    e2 = e.clone(); e2[0] = wl.E
+    assert "routed block" in expect_bad(e2=e2, what="expert out of range")
+    e3 = e.clone(); e3[ntp // B] = 0
+    assert "tail" in expect_bad(e2=e3, what="expert_ids tail")
+    # an extra all-sentinel block appended: num_tokens_padded + B, and the
+    # block names an expert (every entry is a sentinel, so no slot moves)
+    n4 = n.clone(); n4[0] = ntp + B
+    e4 = e.clone(); e4[ntp // B] = int(eh[ntp // B - 1])
+    assert "num_tokens_padded" in expect_bad(e2=e4, n2=n4, what="extra sentinel block")
+    # num_tokens_padded off a block multiple, or one block short
+    n2 = n.clone(); n2[0] = ntp + 1
+    expect_bad(n2=n2, what="not a block multiple")
+    n3 = n.clone(); n3[0] = ntp - B
+    expect_bad(n2=n3, what="drops a block")
+    # a topk id outside [-1, E)
+    ids2 = d_ids.clone(); ids2[0, 0] = wl.E + 3
+    assert "outside" in expect_bad(ids2=ids2, what="id out of range")
+    # and the untouched buffers still pass
+    qma.qma_validate_routing(d_ids, T, topk, wl.E, B, s, e, n, cap)
 
 
 def test_validate_contiguous(gpu):

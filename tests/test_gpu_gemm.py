@@ -701,3 +701,39 @@ def test_grouped_with_no_valid_rows_writes_nothing(gpu):
     a3 = inputs.bf16_normal(rng, (E, 64, K))
     got = masked(a3, np.zeros(E, np.int32), 32, w, s)
     assert np.all(got == SENT)
+
+
+# ---- pipeline depth: bit-identical output --------------------------------
+# The number of K chunks in flight only changes when loads are issued, not
+# the order in which each output's products are summed, so every depth must
+# give the same bits ([announce] scheduling section and [release] indexed
+# techniques: the pipelined main loop keeps the output bit-identical).
+DEPTH_PLANS = [  # small-M overrides that reach gemm_small_m_kernel<1, 4, WK, D>
+    {"block_n": 128, "waves_k": 2, "split_k": 1},
+    {"block_n": 64, "waves_k": 4, "split_k": 1},
+    {"block_n": 256, "waves_k": 1, "split_k": 2},
+]
+
+
+@pytest.mark.parametrize("plan_i", range(len(DEPTH_PLANS)))
+@pytest.mark.parametrize("integer", [True, False])
+def test_pipeline_depth_bit_identical(gpu, plan_i, integer):
+    E, T, topk, K, N = 5, 60, 2, 2048, 512
+    rng = np.random.default_rng(300 + plan_i + 10 * integer)
+    w, s = weights(rng, E, N, K, integer)
+    a = bf16_small_ints(rng, (T, K)) if integer else inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    base = dict(DEPTH_PLANS[plan_i], kernel=qma.KERNEL_SMALL_M, block_m=16, n_stream=1)
+    outs = []
+    for depth in (256, 384, 512):
+        got, plan = indexed(a, topk, ids, w, s, force_bm=16, override=dict(base, k_depth=depth))
+        assert plan.k_depth == depth
+        outs.append(got)
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    if integer:
+        assert np.array_equal(outs[0][valid], rne(ref[valid]))
+    else:
+        assert_per_expert(outs[0], ref, slot_experts(ids, E), "depth")
+    assert np.all(outs[0][~valid] == SENT)

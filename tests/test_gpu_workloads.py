@@ -1,7 +1,14 @@
-"""Full-size workloads through the same calls the benchmark times, checked on
-sampled outputs the oracle computes one by one (gate_up, the activation and
-down, each on the GPU's own input to that stage, plus a fully chained
-sample). Routing buffers are validated in full."""
+"""Full-size workloads through the same calls the benchmark times, checked
+against the oracle stage by stage, each stage on the GPU's own input to it
+(gate_up, the activation, down), plus a fully chained sample.
+
+* decode-shaped workloads (EP8/EP16/EP32/EP128 decode, the 33..79-row EP8
+  share, TP8, masked): every output element of both GEMMs and the activation;
+* prefill-shaped workloads (EP8 prefill, its span-matched variant,
+  contiguous): every row, and 16 columns of every 256-column block, so that
+  every (row tile, expert, column block) workgroup of the launch is checked.
+
+Routing buffers are validated in full."""
 import numpy as np
 import pytest
 import torch
@@ -13,7 +20,8 @@ from gpu_common import assert_per_expert, rne, slot_experts
 
 pytestmark = pytest.mark.gpu
 
-N_SLOTS, N_COLS, N_CHAIN = 128, 96, 12
+N_CHAIN = 12
+PREFILL = {"ep8_prefill", "ep8_prefill_span", "contiguous"}
 
 
 def _sampled(rng, slot_expert, n_slots):
@@ -30,11 +38,23 @@ def _only(slot_expert, slots):
     return m
 
 
-def check_stages(a_bits, a_row_div, slot_expert, c1, h, c2, w13, s13, w2, s2, rng, what):
+def _block_cols(rng, N, per_block=16, block=256):
+    """per_block random columns from every block of 256 (or the whole of a
+    narrower N), sorted."""
+    if N <= block:
+        return np.arange(N)
+    return np.sort(np.concatenate([b + rng.choice(block, per_block, replace=False)
+                                   for b in range(0, N, block)]))
+
+
+def check_stages(a_bits, a_row_div, slot_expert, c1, h, c2, w13, s13, w2, s2, rng, what,
+                 full=True):
     N1, N2 = w13.shape[1], w2.shape[1]
-    slots = _sampled(rng, slot_expert, N_SLOTS)
-    cols1 = np.sort(rng.choice(N1, N_COLS, replace=False))
-    cols2 = np.sort(rng.choice(N2, N_COLS, replace=False))
+    slots = np.nonzero(slot_expert >= 0)[0]
+    if full:
+        cols1, cols2 = np.arange(N1), np.arange(N2)
+    else:
+        cols1, cols2 = _block_cols(rng, N1), _block_cols(rng, N2)
     se = _only(slot_expert, slots)
     ref1 = O.moe_gemm_by_slot(a_bits, a_row_div, se, w13, s13, cols=cols1)
     assert_per_expert(c1[slots][:, cols1], ref1[slots], se[slots], f"{what} gate_up")
@@ -46,7 +66,7 @@ def check_stages(a_bits, a_row_div, slot_expert, c1, h, c2, w13, s13, w2, s2, rn
     ref2 = O.moe_gemm_by_slot(h, 1, se, w2, s2, cols=cols2)
     assert_per_expert(c2[slots][:, cols2], ref2[slots], se[slots], f"{what} down")
     # chained: oracle gate_up rows rounded to bf16, oracle activation, oracle down
-    cs = slots[:N_CHAIN]
+    cs = _sampled(rng, slot_expert, N_CHAIN)[:N_CHAIN]
     sc = _only(slot_expert, cs)
     c1_ref = O.moe_gemm_by_slot(a_bits, a_row_div, sc, w13, s13)
     h_ref = np.zeros(h.shape, np.uint16)
@@ -56,7 +76,7 @@ def check_stages(a_bits, a_row_div, slot_expert, c1, h, c2, w13, s13, w2, s2, rn
 
 
 @pytest.mark.parametrize("name", ["ep8_decode", "tp8", "ep8_prefill", "ep16_decode", "ep32_decode",
-                                  "ep8_prefill_span"])
+                                  "ep8_prefill_span", "ep8_mid", "ep128_decode"])
 def test_indexed_workload(gpu, name):
     wl = inputs.make(name, seed=0)
     rng = np.random.default_rng(1)
@@ -71,7 +91,7 @@ def test_indexed_workload(gpu, name):
                              r.ntp, r.cap)
     c1, h, c2 = (to_host(t, bf16=True) for t in (moe.c1, moe.h, moe.c2))
     check_stages(wl["a"], wl.topk, slot_experts(wl["topk_ids"], wl.E), c1, h, c2, wl["w13"],
-                 wl["s13"], wl["w2"], wl["s2"], rng, name)
+                 wl["s13"], wl["w2"], wl["s2"], rng, name, full=name not in PREFILL)
 
 
 @pytest.mark.parametrize("name", ["contiguous", "masked"])
@@ -97,4 +117,4 @@ def test_grouped_workload(gpu, name):
     torch.cuda.synchronize()
     c1, h, c2 = (to_host(t, bf16=True) for t in (moe.c1, moe.h, moe.c2))
     check_stages(a_rows, 1, row_e, c1, h, c2, wl["w13"], wl["s13"], wl["w2"], wl["s2"], rng,
-                 name)
+                 name, full=name not in PREFILL)

@@ -257,6 +257,20 @@ def test_host_checks_before_any_launch(L):
             qma.qma_indexed_gemm(lay, p0, fake, 64, 2, fake, fake, fake, fake, 1 << 30, 128,
                                  None, fake, stream=0)
         assert e10.value.status == qma.QMA_ERR_INVALID_ARG
+        with pytest.raises(qma.QmaError) as e11:          # GEMM capacity below the bound
+            qma.qma_indexed_gemm(lay, p0, fake, 64, 2, fake, fake, fake, fake, cap - 1, 128,
+                                 None, fake, stream=0)
+        assert e11.value.status == qma.QMA_ERR_INVALID_ARG and "bound" in e11.value.detail
+        # a large-M plan on K = 256 (two chunks of 128) edited to three K
+        # splits: one split would own no chunk, so the host rejects it
+        big = qma.qma_plan_indexed(lay, 64, 2, 128)
+        assert big.kernel == qma.KERNEL_LARGE_M
+        for split in (3, 8):
+            big.split_k = split
+            with pytest.raises(qma.QmaError) as e12:
+                qma.qma_indexed_gemm(lay, big, fake, 64, 2, fake, fake, fake, fake, 1 << 12, 128,
+                                     None, fake, fake, 1 << 30, stream=0)
+            assert e12.value.status == qma.QMA_ERR_INVALID_ARG and "split_k" in e12.value.detail
         # edited plans naming no kernel instance: 8 column tiles per wave,
         # waves_k 3, a streamed 64-column block
         for edit in ({"block_m": 16, "block_n": 128, "waves_k": 4, "split_k": 1},

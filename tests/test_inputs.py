@@ -55,3 +55,13 @@ def test_scales_are_positive_bf16():
     w = inputs.make("tiny", seed=0)
     s = w["s13"]
     assert np.all((s & 0x8000) == 0)                  # |N(0, 0.02)|
+
+
+def test_mid_and_ep128_shares():
+    m = inputs.make("ep8_mid", seed=0, weights=False)
+    c = np.bincount(m["topk_ids"][:, 0], minlength=48)
+    assert m.E == 48 and c.min() >= 40 and c.max() <= 56 and m.T == c.sum()
+    assert (33 <= c).all() and (c < 80).all()          # between decode and large-M
+    e = inputs.make("ep128_decode", seed=0, weights=False)
+    c3 = np.bincount(e["topk_ids"][:, 0], minlength=3)
+    assert e.E == 3 and c3.min() >= 9 and c3.max() <= 15
