@@ -4,19 +4,31 @@
 One step is one pass of the whole hot path over one batch. On the indexed
 path that is moe_align, gate_up, silu_and_mul and down; on the grouped
 paths it is gate_up, silu_and_mul and down. Inputs are resident in HBM
-before timing starts. W warm-up steps run untimed (continued until the step
-has run back to back for --settle-ms, so that the clocks have left their
-idle ramp), then exactly K steps run back to back between device
-synchronisations: that wall time is ms_per_step. K further steps with HIP
-event pairs around every stage, on the launching stream, time each kernel.
-The per-layer gate_up+down time (the pages' kernel-level metric, which
-leaves out routing and activation) is reported next to the whole-step time.
+before timing starts.
 
-`value` is the whole step's effective throughput: algorithmic HBM bytes
-(decode shapes, GB/s) or algorithmic flops (prefill shapes, TFLOP/s)
-divided by ms_per_step. The roofline object covers the gate_up GEMM
-launch. The oracle's CPU time on a bounded sample of the same workload is
-reported as `cpu_baseline`.
+The headline workload (--workload, default the EP8 decode share) gives
+`value`: W warm-up steps run untimed (continued until the step has run back
+to back for --settle-ms, so that the clocks have left their idle ramp), then
+exactly K steps run back to back between device synchronisations; that wall
+time is ms_per_step. K further steps with HIP event pairs around every stage,
+on the launching stream, time each kernel. `value` is the whole step's
+effective throughput: algorithmic HBM bytes (decode shapes, GB/s) or
+algorithmic flops (prefill shapes, TFLOP/s) divided by ms_per_step. The
+roofline object covers the headline workload's gate_up GEMM launch.
+
+The `configs` object repeats the measurement for every workload of the
+pages' scenarios (tiny, EP8 decode, TP8, EP8 prefill, grouped contiguous,
+grouped masked) in the same run: per-kernel event times, the gate_up+down
+pair time (the pages' per-layer kernel metric, which leaves out routing and
+the activation), the pair's rate, roofline fractions per GEMM and for the
+pair, and HBM traffic from the committed rocprofv3 summaries. With flushing
+on (the default), each stage is also timed cold: a 512 MiB device write
+before every timed call evicts the L2s and the MALL.
+
+The oracle's CPU time on a bounded sample of the headline workload is
+reported as `cpu_baseline` (float64, as the oracle stands), with fp32
+timings next to it: per-expert dequantisation included, and matmuls alone on
+cached fp32 weights.
 """
 from __future__ import annotations
 
@@ -26,6 +38,7 @@ import hashlib
 import json
 import os
 import re
+import subprocess
 import sys
 import time
 
@@ -35,7 +48,11 @@ sys.path.insert(0, ROOT)
 METRIC = ("gate_up+down µs/layer; effective HBM GB/s (decode) and TFLOP/s (prefill)")
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-HBM_BOUND = {"ep8_decode", "tp8", "masked", "ep16_decode", "ep32_decode", "tiny"}
+HBM_BOUND = {"ep8_decode", "tp8", "masked", "ep16_decode", "ep32_decode", "tiny", "ep8_mid",
+             "ep128_decode"}
+# the pages' six measured scenarios map onto these workloads
+DEFAULT_CONFIGS = ("tiny", "ep8_decode", "tp8", "ep8_prefill", "contiguous", "masked")
+FLUSH_BYTES = 512 << 20
 
 DESCRIPTIONS = {
     "ep8_decode": "indexed EP8 decode share: 48 experts x U{9..15} rows, hidden 7168, "
@@ -49,6 +66,8 @@ DESCRIPTIONS = {
               "intermediate 2048",
     "ep16_decode": "indexed EP16 decode share: 24 experts x U{9..15} rows",
     "ep32_decode": "indexed EP32 decode share: 12 experts x U{9..15} rows",
+    "ep8_mid": "indexed EP8 share between decode and prefill: 48 experts x U{40..56} rows",
+    "ep128_decode": "indexed EP128 decode share: 3 experts x U{9..15} rows (split-K on)",
     "tiny": "tiny: 8 experts, 64 tokens top-2, K 256, I 128",
 }
 
@@ -92,26 +111,29 @@ def kernel_src_hash():
 
 
 def read_traffic(workload):
-    """HBM traffic of the gate_up launch from a committed rocprofv3 --pmc
-    summary, if it was taken on the current kernel sources."""
+    """HBM traffic per launch of the gate_up and down GEMMs from the committed
+    rocprofv3 --pmc summary, if it was taken on the current kernel sources:
+    {"gate_up": bytes or None, "down": bytes or None}."""
+    out = {"gate_up": None, "down": None}
     path = os.path.join(ROOT, "profiles", f"pmc_gate_up_{workload}.md")
     if not os.path.exists(path):
-        return None
+        return out
     m = re.search(r"qma-traffic: (\{.*\})", open(path).read())
     if not m:
-        return None
+        return out
     d = json.loads(m.group(1))
     if d.get("src_sha") != kernel_src_hash():
-        return None
-    return d.get("bytes_per_launch")
+        return out
+    out["gate_up"] = d.get("bytes_per_launch")
+    out["down"] = d.get("down_bytes_per_launch")
+    return out
 
 
-def cpu_baseline(wl, budget_s):
-    """The oracle as it stands, timed on the host on whole experts of the
-    same workload (gate_up, activation and down per expert) until about
-    budget_s of CPU work; the rate is scaled to the metric's unit."""
-    import numpy as np
-    from oracle import qma_oracle as O
+# --------------------------------------------------------------------------
+# CPU baseline (the oracle, plus plain fp32 NumPy next to it)
+# --------------------------------------------------------------------------
+
+def _blas_info():
     try:
         from threadpoolctl import threadpool_info
         pools = threadpool_info()
@@ -120,22 +142,42 @@ def cpu_baseline(wl, budget_s):
                                  if t.get("user_api") == "blas"})) or "unknown"
     except Exception:                                     # pragma: no cover
         threads, blas = 1, "unknown"
-    E, K, I = wl.E, wl.K, wl.I
+    return threads, blas
+
+
+def _slot_experts(wl):
+    import numpy as np
+    E, K = wl.E, wl.K
     if wl.kind == "indexed":
         se = np.where((wl["topk_ids"] >= 0) & (wl["topk_ids"] < E), wl["topk_ids"], -1)
-        se = se.reshape(-1)
-        a, div = wl["a"], wl.topk
-    elif wl.kind == "contiguous":
-        se, a, div = wl["m_indices"].astype(np.int64), wl["a"], 1
-    else:
-        mm = wl["masked_m"]
-        budget = wl.meta["budget"]
-        se = np.array([[e if r < mm[e] else -1 for r in range(budget)] for e in range(E)])
-        se, a, div = se.reshape(-1), wl["a"].reshape(-1, K), 1
+        return se.reshape(-1), wl["a"], wl.topk
+    if wl.kind == "contiguous":
+        return wl["m_indices"].astype(np.int64), wl["a"], 1
+    mm = wl["masked_m"]
+    budget = wl.meta["budget"]
+    se = np.array([[e if r < mm[e] else -1 for r in range(budget)] for e in range(E)])
+    return se.reshape(-1), wl["a"].reshape(-1, K), 1
+
+
+def _expert_bytes_flops(wl, n):
+    K, I = wl.K, wl.I
+    b = (2 * I * K + K * I) * 9 // 16 + n * (K * 2 + 2 * I * 2 + I * 2 + K * 2)
+    f = 2 * n * 2 * I * K + 2 * n * K * I
+    return b, f
+
+
+def cpu_oracle(wl, budget_s):
+    """The oracle as it stands, timed on the host on whole experts of the
+    same workload (gate_up, activation and down per expert) until about
+    budget_s of CPU work."""
+    import numpy as np
+    from oracle import qma_oracle as O
+    se, a, div = _slot_experts(wl)
+    I = wl.I
     done_bytes = done_flops = 0
     t_total = 0.0
     experts = []
-    for e in range(E):
+    for e in range(wl.E):
         rows = np.nonzero(se == e)[0]
         if rows.size == 0:
             continue
@@ -148,24 +190,106 @@ def cpu_baseline(wl, budget_s):
         hh[rows] = h
         O.moe_gemm_by_slot(hh, 1, only, wl["w2"], wl["s2"])
         t_total += time.perf_counter() - t0
-        n = rows.size
-        done_bytes += (2 * I * K + K * I) * 9 // 16 + n * (K * 2 + 2 * I * 2 + I * 2 + K * 2)
-        done_flops += 2 * n * 2 * I * K + 2 * n * K * I
+        b, f = _expert_bytes_flops(wl, rows.size)
+        done_bytes += b
+        done_flops += f
         experts.append(e)
         if t_total >= budget_s:
             break
-    return t_total, done_bytes, done_flops, threads, experts, blas
+    return t_total, done_bytes, done_flops, experts
 
 
-def host_cpu_model():
+def cpu_fp32(wl, n_experts, reps=3):
+    """Plain fp32 NumPy on the host over the first n_experts experts with
+    rows: gate_up, SiLU-gated activation and down per expert, (i) with the
+    expert's weights dequantised to fp32 inside the timed region, (ii) with
+    them dequantised beforehand (matmuls alone). 1 warm-up + `reps` timed
+    repetitions each; median seconds per repetition."""
+    import numpy as np
+    from oracle import qma_oracle as O
+    se, a, div = _slot_experts(wl)
+    I = wl.I
+    a32 = O.bf16_to_f64(a).astype(np.float32)
+    jobs = []
+    for e in range(wl.E):
+        rows = np.nonzero(se == e)[0]
+        if rows.size:
+            jobs.append((e, rows))
+        if len(jobs) == n_experts:
+            break
+
+    def deq32(qw, sc):
+        q = O.unpack_uint4(qw).astype(np.float32) - np.float32(8)
+        s = O.bf16_to_f64(sc).astype(np.float32)
+        return q * np.repeat(s, 32, axis=-1)
+
+    def layer(x, w13, w2):
+        c1 = x @ w13.T
+        g, u = c1[:, :I], c1[:, I:]
+        h = g / (np.float32(1) + np.exp(-g)) * u
+        return h @ w2.T
+
+    def with_deq():
+        for e, rows in jobs:
+            layer(a32[rows // div], deq32(wl["w13"][e], wl["s13"][e]),
+                  deq32(wl["w2"][e], wl["s2"][e]))
+
+    cached = {e: (deq32(wl["w13"][e], wl["s13"][e]), deq32(wl["w2"][e], wl["s2"][e]))
+              for e, _ in jobs}
+
+    def matmul_only():
+        for e, rows in jobs:
+            layer(a32[rows // div], *cached[e])
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            ts.append(time.perf_counter() - t0)
+        return float(np.median(ts))
+
+    t_deq = timed(with_deq)
+    t_mm = timed(matmul_only)
+    b = f = 0
+    for _, rows in jobs:
+        bb, ff = _expert_bytes_flops(wl, rows.size)
+        b += bb
+        f += ff
+    return t_deq, t_mm, b, f, [e for e, _ in jobs]
+
+
+def host_cpu():
+    info = {"nproc": os.cpu_count()}
     try:
+        fields = {}
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                return line.split(":", 1)[1].strip()
+            k, _, v = line.partition(":")
+            k = k.strip()
+            if k in ("model name", "cpu family", "model", "stepping", "vendor_id") and k not in fields:
+                fields[k] = v.strip()
+        info["model_name"] = fields.get("model name", "unknown")
+        info["vendor"] = fields.get("vendor_id")
+        info["family_model_stepping"] = "%s/%s/%s" % (fields.get("cpu family"), fields.get("model"),
+                                                      fields.get("stepping"))
     except OSError:                                       # pragma: no cover
+        info["model_name"] = "unknown"
+    try:
+        out = subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout
+        for line in out.splitlines():
+            k, _, v = line.partition(":")
+            if k.strip() in ("Model name", "BIOS Model name", "Socket(s)", "Core(s) per socket",
+                             "Thread(s) per core"):
+                info["lscpu " + k.strip()] = v.strip()
+    except Exception:                                     # pragma: no cover
         pass
-    return "unknown"
+    return info
 
+
+# --------------------------------------------------------------------------
+# GPU side
+# --------------------------------------------------------------------------
 
 def practical_roofs(torch, dev):
     """What plain reference work reaches on this GPU, next to the vendor
@@ -175,14 +299,12 @@ def practical_roofs(torch, dev):
     last two through the vendor GEMM library via torch. All are measured
     after the timed region, back to back with a settle, and serve as context
     only; none is on the product path."""
-    import time as _t
-
     def run(fn, n):
         for _ in range(3):
             fn()
         torch.cuda.synchronize()
-        t0 = _t.perf_counter()
-        while _t.perf_counter() - t0 < 0.2:
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < 0.2:
             fn()
             torch.cuda.synchronize()
         e0 = torch.cuda.Event(enable_timing=True)
@@ -199,8 +321,6 @@ def practical_roofs(torch, dev):
     dst = torch.empty_like(src)
     t_copy = run(lambda: dst.copy_(src), 20)
     del src, dst
-    # read-bound: 16 bf16 token rows against a 1 GiB bf16 weight matrix
-    # (the vendor GEMM library's skinny product reads the matrix once)
     kk, nn = 16384, 32768
     wg = torch.empty(nn, kk, dtype=torch.bfloat16, device=dev).fill_(0.5)
     xg = torch.randn(16, kk, device=dev).to(torch.bfloat16)
@@ -218,19 +338,213 @@ def practical_roofs(torch, dev):
                     "(weight reads); dense 8192^3 bf16 matmul; all via torch"}
 
 
+class WeightCache:
+    """Host arrays and prepacked device weights per (E, K, I, seed): the EP8
+    decode, EP8 prefill, contiguous and masked workloads share one EP8 weight
+    set (same shapes, same seed), generated and packed once."""
+
+    def __init__(self):
+        self.host = {}
+        self.dev = {}
+
+    def attach(self, wl, seed):
+        from quantized_moe_align_amd import inputs
+        key = (wl.E, wl.K, wl.I, seed)
+        if key not in self.host:
+            full = inputs._with_weights(inputs.Workload(wl.name, wl.kind, wl.E, wl.K, wl.I),
+                                        seed, True)
+            self.host[key] = {k: full[k] for k in ("w13", "s13", "w2", "s2")}
+        wl.arrays.update(self.host[key])
+        return key
+
+    def packed(self, key, path):
+        from quantized_moe_align_amd import qma
+        from quantized_moe_align_amd.moe import ExpertWeights
+        if key not in self.dev:
+            h = self.host[key]
+            self.dev[key] = {qma.PATH_INDEXED: (ExpertWeights(h["w13"], h["s13"]),
+                                                ExpertWeights(h["w2"], h["s2"]))}
+        d = self.dev[key]
+        if path not in d:
+            base13, base2 = d[qma.PATH_INDEXED]
+            d[path] = (base13.with_path(path), base2.with_path(path))
+        return d[path]
+
+
+def build_runner(name, seed, cache, schedule, overrides):
+    """Inputs on the device and the step's stages for one workload."""
+    import torch
+    from quantized_moe_align_amd import inputs, qma
+    from quantized_moe_align_amd.moe import GroupedMoE, IndexedMoE, to_device, workspace_for
+
+    wl = inputs.make(name, seed=seed, weights=False)
+    key = cache.attach(wl, seed)
+    work = algorithmic_work(wl)
+    if wl.kind == "indexed":
+        w13, w2 = cache.packed(key, qma.PATH_INDEXED)
+        moe = IndexedMoE(w13, w2, wl.T, wl.topk)
+        a = to_device(wl["a"])
+        ids = to_device(wl["topk_ids"])
+        stages = [("moe_align", lambda: moe.align(ids)), ("gate_up", lambda: moe.gate_up(a)),
+                  ("silu_and_mul", moe.act), ("down", lambda: moe.down())]
+    else:
+        path = (qma.PATH_GROUPED_CONTIGUOUS if wl.kind == "contiguous"
+                else qma.PATH_GROUPED_MASKED)
+        w13, w2 = cache.packed(key, path)
+        if wl.kind == "contiguous":
+            index = to_device(wl["m_indices"])
+            moe = GroupedMoE(w13, w2, wl["m_indices"].size)
+        else:
+            index = to_device(wl["masked_m"])
+            moe = GroupedMoE(w13, w2, wl.meta["budget"], wl.meta["expected_m"])
+        a = to_device(wl["a"])
+        stages = [("gate_up", lambda: moe.gate_up(a, index)), ("silu_and_mul", moe.act),
+                  ("down", lambda: moe.down(index))]
+    applied = (False, False)
+    if schedule == "dynamic":
+        applied = moe.set_schedule(qma.SCHEDULE_DYNAMIC)
+    for which, ov in (("13", overrides.get("gate_up")), ("2", overrides.get("down"))):
+        if ov:
+            plan = getattr(moe, "plan" + which)
+            for k, v in ov.items():
+                setattr(plan, k, v)
+            setattr(moe, "ws" + which, workspace_for(plan))
+    torch.cuda.synchronize()
+    return {"name": name, "wl": wl, "work": work, "moe": moe, "stages": stages,
+            "schedule": applied}
+
+
+def measure(r, steps, warmup, settle_ms, idle_gap_ms=0.0, flush=None):
+    """ms_per_step over K back-to-back steps, per-stage event times over K
+    more steps, and (with a flush buffer) per-stage times with a 512 MiB
+    device write before every timed call."""
+    import numpy as np
+    import torch
+    stages = r["stages"]
+    stream = torch.cuda.current_stream()
+    t_w = time.perf_counter()
+    n_warm = 0
+    while n_warm < warmup or (time.perf_counter() - t_w) * 1e3 < settle_ms:
+        for _ in range(10 if n_warm >= warmup else 1):
+            for _, fn in stages:
+                fn()
+            n_warm += 1
+        if n_warm >= warmup:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+    def timed_steps(per_stage, flush_buf=None):
+        pairs = [(name, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                 for _ in range(steps) for name, _ in stages] if per_stage else []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        i = 0
+        for s in range(steps):
+            if idle_gap_ms > 0:
+                torch.cuda.synchronize()
+                time.sleep(idle_gap_ms * 1e-3)
+            for name, fn in stages:
+                if flush_buf is not None:
+                    flush_buf.fill_(s * 8 + i % 8)
+                if per_stage:
+                    pairs[i][1].record(stream)
+                fn()
+                if per_stage:
+                    pairs[i][2].record(stream)
+                i += 1
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, pairs
+
+    # the timed region: exactly K steps, launched back to back
+    wall, _ = timed_steps(per_stage=False)
+    out = {"ms_per_step": wall / steps * 1e3}
+
+    def collect(pairs):
+        ev = {name: [] for name, _ in stages}
+        for name, e0, e1 in pairs:
+            ev[name].append(e0.elapsed_time(e1) * 1e3)       # us
+        return ev
+
+    _, pairs = timed_steps(per_stage=True)
+    out["ev"] = collect(pairs)
+    if flush is not None:
+        _, fpairs = timed_steps(per_stage=True, flush_buf=flush)
+        out["ev_flushed"] = collect(fpairs)
+    if idle_gap_ms > 0:
+        out["ms_per_step"] = sum(float(np.median(v)) for v in out["ev"].values()) * 1e-3
+    return out
+
+
+def pair_report(name, work, ev, traffic):
+    """gate_up, down and pair times with rates and roofline fractions."""
+    import numpy as np
+    hbm = name in HBM_BOUND
+    mean = {k: float(np.mean(v)) for k, v in ev.items()}
+    med = {k: float(np.median(v)) for k, v in ev.items()}
+    gu, dn = mean["gate_up"], mean["down"]
+    rep = {"us_mean": {k: round(v, 2) for k, v in mean.items()},
+           "us_median": {k: round(v, 2) for k, v in med.items()},
+           "pair_us": round(gu + dn, 2), "pair_us_median": round(med["gate_up"] + med["down"], 2)}
+    if hbm:
+        def rate(b, us):
+            return b / (us * 1e-6) / 1e9
+        rg, rd = rate(work["gate_up_bytes"], gu), rate(work["down_bytes"], dn)
+        rp = rate(work["gate_up_bytes"] + work["down_bytes"], gu + dn)
+        rep.update({"bound": "hbm", "unit": "GB/s", "pair_rate": round(rp, 1),
+                    "gate_up_rate": round(rg, 1), "down_rate": round(rd, 1),
+                    "frac": {"gate_up": round(rg / HBM_PEAK_GBS, 4),
+                             "down": round(rd / HBM_PEAK_GBS, 4),
+                             "pair": round(rp / HBM_PEAK_GBS, 4)}})
+    else:
+        def rate(f, us):
+            return f / (us * 1e-6) / 1e12
+        rg, rd = rate(work["gate_up_flops"], gu), rate(work["down_flops"], dn)
+        rp = rate(work["gate_up_flops"] + work["down_flops"], gu + dn)
+        rep.update({"bound": "mfma", "unit": "TFLOP/s", "pair_rate": round(rp, 2),
+                    "gate_up_rate": round(rg, 2), "down_rate": round(rd, 2),
+                    "frac": {"gate_up": round(rg / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "down": round(rd / MFMA_BF16_PEAK_TFLOPS, 4),
+                             "pair": round(rp / MFMA_BF16_PEAK_TFLOPS, 4)}})
+    if traffic is not None:
+        rep["traffic_bytes"] = traffic
+        rep["traffic_over_algorithmic"] = {
+            k: (round(traffic[k] / work[k + "_bytes"], 3) if traffic.get(k) else None)
+            for k in ("gate_up", "down")}
+    return rep
+
+
+def plan_brief(plan):
+    d = plan.as_dict()
+    return {k: d[k] for k in ("kernel", "block_m", "block_n", "split_k", "k_depth", "waves_k",
+                              "n_stream", "schedule")}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ep8_decode", choices=sorted(DESCRIPTIONS))
+    ap.add_argument("--workload", default="ep8_decode", choices=sorted(DESCRIPTIONS),
+                    help="the headline workload that gives `value` and `roofline`")
+    ap.add_argument("--configs", default="default",
+                    help="workloads measured into the `configs` object: 'default' (the "
+                         "pages' scenarios: %s), 'none', or a comma-separated list"
+                         % ", ".join(DEFAULT_CONFIGS))
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-budget", type=float, default=15.0,
-                    help="seconds of oracle CPU work for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle CPU work for cpu_baseline (0 = skip the CPU legs)")
+    ap.add_argument("--cpu-fp32-experts", type=int, default=4,
+                    help="experts in the fp32 NumPy legs of cpu_baseline")
     ap.add_argument("--schedule", default="semi_static", choices=("semi_static", "dynamic"),
                     help="how small-M GEMMs hand out (tile, column block) work; dynamic "
                          "applies where the plan accepts it (16/32-row tiles, one K "
                          "partition)")
+    ap.add_argument("--override-gate-up", default="",
+                    help="JSON object of plan fields to set on the headline workload's "
+                         "gate_up plan before timing (A/B runs, e.g. '{\"split_k\": 1}')")
+    ap.add_argument("--override-down", default="", help="the same for the down plan")
+    ap.add_argument("--no-flush", dest="flush", action="store_false",
+                    help="skip the cold timings (a 512 MiB device write before each call)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a buffer of this many bytes 3 times (a "
                          "plain copy kernel of known size, to calibrate rocprofv3 "
@@ -250,98 +564,40 @@ def main():
                           "pair is one rank's share and has no cross-GPU step; "
                           f"--gpus {args.gpus} is not supported"}))
         sys.exit(2)
+    if args.configs == "default":
+        configs = list(DEFAULT_CONFIGS)
+    elif args.configs == "none":
+        configs = []
+    else:
+        configs = [c for c in args.configs.split(",") if c]
+        for c in configs:
+            if c not in DESCRIPTIONS:
+                ap.error(f"unknown config {c}")
+    overrides = {"gate_up": json.loads(args.override_gate_up) if args.override_gate_up else {},
+                 "down": json.loads(args.override_down) if args.override_down else {}}
 
     import numpy as np
     import torch
-    from quantized_moe_align_amd import inputs, qma
-    from quantized_moe_align_amd.moe import (ExpertWeights, GroupedMoE, IndexedMoE, to_device)
+    from quantized_moe_align_amd import qma
 
     qma.lib()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = inputs.make(args.workload, seed=args.seed)
-    work = algorithmic_work(wl)
+    cache = WeightCache()
+    flush = (torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+             if args.flush and configs else None)
 
-    if wl.kind == "indexed":
-        w13 = ExpertWeights(wl["w13"], wl["s13"])
-        w2 = ExpertWeights(wl["w2"], wl["s2"])
-        moe = IndexedMoE(w13, w2, wl.T, wl.topk)
-        a = to_device(wl["a"])
-        ids = to_device(wl["topk_ids"])
-        stages = [("moe_align", lambda: moe.align(ids)), ("gate_up", lambda: moe.gate_up(a)),
-                  ("silu_and_mul", moe.act), ("down", lambda: moe.down())]
-    else:
-        path = (qma.PATH_GROUPED_CONTIGUOUS if wl.kind == "contiguous"
-                else qma.PATH_GROUPED_MASKED)
-        w13 = ExpertWeights(wl["w13"], wl["s13"], path)
-        w2 = ExpertWeights(wl["w2"], wl["s2"], path)
-        if wl.kind == "contiguous":
-            index = to_device(wl["m_indices"])
-            moe = GroupedMoE(w13, w2, wl["m_indices"].size)
-        else:
-            index = to_device(wl["masked_m"])
-            moe = GroupedMoE(w13, w2, wl.meta["budget"], wl.meta["expected_m"])
-        a = to_device(wl["a"])
-        stages = [("gate_up", lambda: moe.gate_up(a, index)), ("silu_and_mul", moe.act),
-                  ("down", lambda: moe.down(index))]
-    sched_applied = (False, False)
-    if args.schedule == "dynamic":
-        sched_applied = moe.set_schedule(qma.SCHEDULE_DYNAMIC)
-    stream = torch.cuda.current_stream()
-
-    # Warm-up: W steps, continued (untimed) until the GPU has run the step
-    # back-to-back for at least --settle-ms. From idle, the clocks take some
-    # tens of ms to reach their sustained level; steps timed inside that
-    # ramp measure the power state, not the kernels.
-    t_w = time.perf_counter()
-    n_warm = 0
-    while n_warm < args.warmup or (time.perf_counter() - t_w) * 1e3 < args.settle_ms:
-        for _ in range(10 if n_warm >= args.warmup else 1):
-            for _, fn in stages:
-                fn()
-            n_warm += 1
-        if n_warm >= args.warmup:
-            torch.cuda.synchronize()
-    torch.cuda.synchronize()
-
-    def timed_steps(per_stage: bool):
-        """K steps between device synchronisations; with per_stage, an event
-        pair around every stage (each record adds a few us of launch gap)."""
-        pairs = [(name, torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                 for _ in range(args.steps) for name, _ in stages] if per_stage else []
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        i = 0
-        for _ in range(args.steps):
-            if args.idle_gap_ms > 0:
-                torch.cuda.synchronize()
-                time.sleep(args.idle_gap_ms * 1e-3)
-            for name, fn in stages:
-                if per_stage:
-                    pairs[i][1].record(stream)
-                fn()
-                if per_stage:
-                    pairs[i][2].record(stream)
-                i += 1
-        torch.cuda.synchronize()
-        return time.perf_counter() - t0, pairs
-
-    # The timed region: exactly K steps, launched back to back.
-    wall, _ = timed_steps(per_stage=False)
-    ms_per_step = wall / args.steps * 1e3
-    # Per-kernel times: K more steps with events around every stage.
-    _, pairs = timed_steps(per_stage=True)
-    ev = {name: [] for name, _ in stages}
-    for name, e0, e1 in pairs:
-        ev[name].append(e0.elapsed_time(e1) * 1e3)          # us
+    # headline workload
+    r = build_runner(args.workload, args.seed, cache, args.schedule, overrides)
+    m = measure(r, args.steps, args.warmup, args.settle_ms, args.idle_gap_ms)
+    work, moe, ev = r["work"], r["moe"], m["ev"]
+    ms_per_step = m["ms_per_step"]
     us = {k: float(np.mean(v)) for k, v in ev.items()}
     med = {k: float(np.median(v)) for k, v in ev.items()}
-    if args.idle_gap_ms > 0:
-        ms_per_step = sum(med.values()) * 1e-3
-
     hbm = args.workload in HBM_BOUND
     total_bytes = work["gate_up_bytes"] + work["down_bytes"]
     total_flops = work["gate_up_flops"] + work["down_flops"]
+    traffic = read_traffic(args.workload)
     if hbm:
         value = total_bytes / (ms_per_step * 1e-3) / 1e9
         unit = "GB/s"
@@ -354,18 +610,12 @@ def main():
         achieved = work["gate_up_flops"] / (us["gate_up"] * 1e-6) / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
-    roof["traffic"] = read_traffic(args.workload)
+    roof["traffic"] = traffic["gate_up"]
     roof["kernel"] = "gate_up GEMM (" + ("small-M" if moe.plan13.kernel == 1 else "large-M") + ")"
-
-    cpu = None
-    if args.cpu_budget > 0:
-        t_cpu, b_cpu, f_cpu, threads, experts, blas = cpu_baseline(wl, args.cpu_budget)
-        cpu = {"value": round((b_cpu / t_cpu / 1e9) if hbm else (f_cpu / t_cpu / 1e12), 4),
-               "unit": unit, "cores": threads, "kind": "oracle",
-               "host": {"cpu": host_cpu_model(), "nproc": os.cpu_count(), "blas": blas},
-               "sample": f"experts {experts[0]}..{experts[-1]} ({len(experts)} of "
-                         f"{work['experts_with_rows']}) of the same workload: gate_up, "
-                         f"activation and down per expert in float64, {t_cpu:.1f} s"}
+    sched = r["schedule"]
+    headline_plan = {"gate_up": moe.plan13.as_dict(), "down": moe.plan2.as_dict()}
+    wl_main = r["wl"]
+    del r, moe
 
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": unit, "n_gpus": 1,
@@ -376,8 +626,9 @@ def main():
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload,
                    "rows": work["rows"], "weights": "uint4 group-32 bf16 scales, zero point 8",
                    "parallelism": "one EP/TP rank's share on one GPU",
-                   "schedule": {"gate_up": "dynamic" if sched_applied[0] else "semi_static",
-                                "down": "dynamic" if sched_applied[1] else "semi_static"},
+                   "schedule": {"gate_up": "dynamic" if sched[0] else "semi_static",
+                                "down": "dynamic" if sched[1] else "semi_static"},
+                   **({"plan_overrides": overrides} if any(overrides.values()) else {}),
                    **({"idle_gap_ms": args.idle_gap_ms} if args.idle_gap_ms > 0 else {})},
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
         "kernel_us_mean": {k: round(v, 2) for k, v in us.items()},
@@ -389,10 +640,50 @@ def main():
                                 "TFLOP/s": round(total_flops / ((us["gate_up"] + us["down"])
                                                                 * 1e-6) / 1e12, 2)},
         "algorithmic": work,
-        "plan": {"gate_up": moe.plan13.as_dict(), "down": moe.plan2.as_dict()},
+        "plan": headline_plan,
         "roofline": roof,
-        "cpu_baseline": cpu,
     }
+
+    # every scenario of the pages, measured in the same run
+    if configs:
+        cfg_out = {}
+        for name in configs:
+            rc = build_runner(name, args.seed, cache, "semi_static", {})
+            mc = measure(rc, args.steps, args.warmup, min(args.settle_ms, 150.0), flush=flush)
+            rep = pair_report(name, rc["work"], mc["ev"], read_traffic(name))
+            rep["ms_per_step"] = round(mc["ms_per_step"], 4)
+            rep["workload"] = DESCRIPTIONS[name]
+            rep["plan"] = {"gate_up": plan_brief(rc["moe"].plan13),
+                           "down": plan_brief(rc["moe"].plan2)}
+            if "ev_flushed" in mc:
+                f = pair_report(name, rc["work"], mc["ev_flushed"], None)
+                rep["flushed"] = {k: f[k] for k in ("us_mean", "pair_us", "pair_rate", "frac")}
+            cfg_out[name] = rep
+            del rc
+            torch.cuda.synchronize()
+        out["configs"] = cfg_out
+
+    if args.cpu_budget > 0:
+        threads, blas = _blas_info()
+        t_cpu, b_cpu, f_cpu, experts = cpu_oracle(wl_main, args.cpu_budget)
+        t_deq, t_mm, b32, f32, ex32 = cpu_fp32(wl_main, args.cpu_fp32_experts)
+
+        def rate(b, f, t):
+            return round((b / t / 1e9) if hbm else (f / t / 1e12), 4)
+        out["cpu_baseline"] = {
+            "value": rate(b_cpu, f_cpu, t_cpu), "unit": unit, "cores": threads, "kind": "oracle",
+            "host": {**host_cpu(), "blas": blas},
+            "sample": f"experts {experts[0]}..{experts[-1]} ({len(experts)} of "
+                      f"{work['experts_with_rows']}) of the same workload: gate_up, activation "
+                      f"and down per expert in float64 (the oracle), {t_cpu:.1f} s",
+            "fp32": {"with_dequant": rate(b32, f32, t_deq), "matmul_only": rate(b32, f32, t_mm),
+                     "unit": unit,
+                     "sample": f"experts {ex32[0]}..{ex32[-1]} ({len(ex32)}), NumPy fp32 "
+                               f"gate_up, SiLU-gated activation and down; median of 3 after "
+                               f"1 warm-up: {t_deq:.2f} s with per-expert dequantisation, "
+                               f"{t_mm:.3f} s on cached fp32 weights"}}
+    else:
+        out["cpu_baseline"] = None
     if args.roofs:
         out["practical_roofs"] = practical_roofs(torch, dev)
     if args.copy_bytes > 0:

@@ -52,6 +52,18 @@ class ExpertWeights:
         torch.cuda.current_stream().synchronize()
         del qw, sc
 
+    def with_path(self, path: int) -> "ExpertWeights":
+        """The same prepacked weights under a layer handle of another routing
+        family (one packed layout serves every family, so nothing is packed
+        again)."""
+        other = ExpertWeights.__new__(ExpertWeights)
+        other.E, other.N, other.K, other.path = self.E, self.N, self.K, path
+        other.layer = qma.qma_layer_create(self.E, self.N, self.K, path)
+        if qma.qma_packed_weight_bytes(other.layer) != self.packed.numel():
+            raise ValueError("packed sizes differ between paths")
+        other.packed = self.packed
+        return other
+
     @property
     def info(self):
         return qma.qma_layer_info(self.layer)
