@@ -301,6 +301,29 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
                             const float* topk_weights, uint16_t* c, void* ws,
                             size_t ws_bytes, void* stream);
 
+/* qma_indexed_gemm for callers that cannot allocate device memory: code
+ * under hipGraph capture, tight serving loops, harnesses that forbid
+ * allocation. Same arguments, results and errors as qma_indexed_gemm, minus
+ * the workspace: a plan that needs one (split-K partials, the dynamic
+ * schedule's counter) uses the library's static device scratch, a fixed
+ * 32 MiB array that every device the library runs on holds until the
+ * process ends. A plan needing more than 32 MiB (qma_workspace_bytes) ->
+ * QMA_ERR_WORKSPACE before any launch. The call allocates nothing; the
+ * first call on a device looks up that device's scratch address. All calls
+ * on one device share its scratch, and the scratch keeps the last call's
+ * contents (the kernels write every partial they read and reset the
+ * counter themselves): calls that overlap on one device, on different
+ * streams or threads, race on it and must be serialised by the caller. */
+qma_status qma_indexed_gemm_scratch(const qma_layer_t* layer, const qma_plan_t* plan,
+                                    const uint16_t* a, int32_t a_rows,
+                                    int32_t a_row_div, const void* packed_w,
+                                    const int32_t* sorted_ids,
+                                    const int32_t* expert_ids,
+                                    const int32_t* num_tokens_padded,
+                                    int32_t sorted_cap, int32_t num_slots,
+                                    const float* topk_weights, uint16_t* c,
+                                    void* stream);
+
 /* Grouped contiguous GEMM ([release] grouped techniques: contiguous
  * prefill pads each expert to 128 rows). c[r] = a[r] . W[m_indices[r]]^T
  * for rows with m_indices[r] >= 0.

@@ -630,6 +630,31 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
   return hip_status(qma::launch_gemm(g, stream), "indexed gemm launch");
 }
 
+qma_status qma_indexed_gemm_scratch(const qma_layer_t* layer, const qma_plan_t* plan,
+                                    const uint16_t* a, int32_t a_rows, int32_t a_row_div,
+                                    const void* packed_w, const int32_t* sorted_ids,
+                                    const int32_t* expert_ids, const int32_t* num_tokens_padded,
+                                    int32_t sorted_cap, int32_t num_slots,
+                                    const float* topk_weights, uint16_t* c, void* stream) {
+  qma_status s = check_layer_plan(layer, plan, QMA_PATH_INDEXED);
+  if (s != QMA_OK) return s;
+  if (num_slots < 0) return fail(QMA_ERR_INVALID_ARG, "bad sizes");
+  const size_t need = ws_bytes_for(plan, num_slots);
+  if (need > qma::kScratchBytes)
+    return fail(QMA_ERR_WORKSPACE,
+                "this plan needs %zu bytes of workspace; the static scratch holds %zu "
+                "(call qma_indexed_gemm with a workspace instead)",
+                need, qma::kScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    const int err = qma::scratch_device_ptr(&ws);
+    if (err != 0) return hip_status(err, "static scratch address");
+  }
+  return qma_indexed_gemm(layer, plan, a, a_rows, a_row_div, packed_w, sorted_ids, expert_ids,
+                          num_tokens_padded, sorted_cap, num_slots, topk_weights, c, ws, need,
+                          stream);
+}
+
 qma_status qma_grouped_contiguous_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
                                        const uint16_t* a, const int32_t* m_indices,
                                        int32_t M, const void* packed_w, uint16_t* c,

@@ -33,6 +33,9 @@ constexpr int kStreamChunks = 8;
 constexpr int kStreamTargetChunks = 14;
 // bytes at the end of the workspace holding a dynamic schedule's counter
 constexpr int kWorkCounterBytes = 256;
+// size of the library's static device scratch (qma_indexed_gemm_scratch):
+// the split-K partials and the work counter of one call
+constexpr size_t kScratchBytes = (size_t)32 << 20;
 
 struct Layer {
   int32_t E, N, K;
@@ -88,6 +91,9 @@ int launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t topk,
 int launch_combine(const uint16_t* c2, const float* w, const int32_t* ids,
                    int32_t E, int32_t T, int32_t topk, int32_t N,
                    uint16_t* out, void* stream);
+// Device address of the static scratch on the current device (looked up once
+// per device); returns a hipError_t as int.
+int scratch_device_ptr(void** out);
 
 }  // namespace qma
 

@@ -7,7 +7,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "qma_internal.h"
@@ -1036,6 +1038,38 @@ __global__ __launch_bounds__(256, 3) void gemm_small_m_xs_dyn_kernel(const GemmP
 
 __global__ void reset_counter_kernel(int32_t* c) {
   if (threadIdx.x == 0) *c = 0;
+}
+
+// Static device scratch for callers that cannot allocate: every device the
+// library runs on holds its own copy until the process ends. In host code the
+// name below is only a stand-in for the symbol, never a device address; the
+// address is looked up per device with hipGetSymbolAddress and only that
+// pointer is handed to kernels.
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxScratchDevices = 64;
+
+int scratch_device_ptr(void** out) {
+  static std::atomic<void*> ptrs[kMaxScratchDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return (int)e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return (int)hipErrorInvalidDevice;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      // the device is current here, so this is its copy of the array
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return (int)e;
+      if (!p) return (int)hipErrorInvalidSymbol;
+      ptrs[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return 0;
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {

@@ -31,7 +31,7 @@ EXPORTS = (
     "qma_packed_weight_bytes", "qma_prepack", "qma_plan_indexed",
     "qma_plan_grouped", "qma_workspace_bytes", "qma_align_sizes",
     "qma_moe_align", "qma_validate_routing", "qma_validate_contiguous",
-    "qma_indexed_gemm", "qma_grouped_contiguous_gemm",
+    "qma_indexed_gemm", "qma_indexed_gemm_scratch", "qma_grouped_contiguous_gemm",
     "qma_grouped_masked_gemm", "qma_silu_and_mul", "qma_moe_combine", "qma_router_topk",
     "qma_status_str", "qma_last_error_detail", "qma_version",
 )
@@ -96,6 +96,8 @@ def lib():
             "qma_validate_contiguous": (I32, [P, I32, I32, P]),
             "qma_indexed_gemm": (I32, [P, ctypes.POINTER(Plan), P, I32, I32, P, P, P, P,
                                        I32, I32, P, P, P, SZ, P]),
+            "qma_indexed_gemm_scratch": (I32, [P, ctypes.POINTER(Plan), P, I32, I32, P, P, P,
+                                               P, I32, I32, P, P, P]),
             "qma_grouped_contiguous_gemm": (I32, [P, ctypes.POINTER(Plan), P, P, I32, P, P,
                                                   P, SZ, P]),
             "qma_grouped_masked_gemm": (I32, [P, ctypes.POINTER(Plan), P, P, I32, I32, P,
@@ -219,6 +221,16 @@ def qma_indexed_gemm(layer, plan: Plan, a, a_rows, a_row_div, packed_w, sorted_i
                                   _ptr(num_tokens_padded), sorted_cap, num_slots,
                                   _ptr(topk_weights), _ptr(c), _ptr(ws), ws_bytes,
                                   _stream(stream)))
+
+
+def qma_indexed_gemm_scratch(layer, plan: Plan, a, a_rows, a_row_div, packed_w, sorted_ids,
+                             expert_ids, num_tokens_padded, sorted_cap, num_slots, topk_weights,
+                             c, stream=None) -> None:
+    _check(lib().qma_indexed_gemm_scratch(layer, ctypes.byref(plan), _ptr(a), a_rows,
+                                          a_row_div, _ptr(packed_w), _ptr(sorted_ids),
+                                          _ptr(expert_ids), _ptr(num_tokens_padded),
+                                          sorted_cap, num_slots, _ptr(topk_weights), _ptr(c),
+                                          _stream(stream)))
 
 
 def qma_grouped_contiguous_gemm(layer, plan: Plan, a, m_indices, M, packed_w, c,
