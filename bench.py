@@ -22,8 +22,10 @@ grouped masked) in the same run: per-kernel event times, the gate_up+down
 pair time (the pages' per-layer kernel metric, which leaves out routing and
 the activation), the pair's rate, roofline fractions per GEMM and for the
 pair, and HBM traffic from the committed rocprofv3 summaries. With flushing
-on (the default), each stage is also timed cold: a 512 MiB device write
-before every timed call evicts the L2s and the MALL.
+on (the default), each stage is also timed cold: a 512 MiB device read
+before every timed call evicts the L2s and the MALL. (A write would leave
+up to the MALL's size of dirty lines, whose write-back then competes with
+the timed kernel's reads.)
 
 The oracle's CPU time on a bounded sample of the headline workload is
 reported as `cpu_baseline` (float64, as the oracle stands), with fp32
@@ -417,7 +419,7 @@ def build_runner(name, seed, cache, schedule, overrides):
 def measure(r, steps, warmup, settle_ms, idle_gap_ms=0.0, flush=None):
     """ms_per_step over K back-to-back steps, per-stage event times over K
     more steps, and (with a flush buffer) per-stage times with a 512 MiB
-    device write before every timed call."""
+    device read before every timed call."""
     import numpy as np
     import torch
     stages = r["stages"]
@@ -445,7 +447,7 @@ def measure(r, steps, warmup, settle_ms, idle_gap_ms=0.0, flush=None):
                 time.sleep(idle_gap_ms * 1e-3)
             for name, fn in stages:
                 if flush_buf is not None:
-                    flush_buf.fill_(s * 8 + i % 8)
+                    flush_buf.max()          # reads 512 MiB: evicts with clean lines
                 if per_stage:
                     pairs[i][1].record(stream)
                 fn()
@@ -544,7 +546,7 @@ def main():
                          "gate_up plan before timing (A/B runs, e.g. '{\"split_k\": 1}')")
     ap.add_argument("--override-down", default="", help="the same for the down plan")
     ap.add_argument("--no-flush", dest="flush", action="store_false",
-                    help="skip the cold timings (a 512 MiB device write before each call)")
+                    help="skip the cold timings (a 512 MiB device read before each call)")
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="after the run, copy a buffer of this many bytes 3 times (a "
                          "plain copy kernel of known size, to calibrate rocprofv3 "
@@ -584,7 +586,7 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     cache = WeightCache()
-    flush = (torch.empty(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
+    flush = (torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device=dev)
              if args.flush and configs else None)
 
     # headline workload
