@@ -92,8 +92,19 @@ typedef enum qma_kernel {
    * decode swaps the MMA operands). HBM-bound. */
   QMA_KERNEL_SMALL_M = 1,
   /* Many rows per expert (prefill): token tiles staged in LDS, weights
-   * dequantised into the MFMA column side. MFMA-bound. */
-  QMA_KERNEL_LARGE_M = 2
+   * dequantised into the MFMA column side. MFMA-bound. Every wave loads,
+   * dequantises and multiplies; takes split-K. */
+  QMA_KERNEL_LARGE_M = 2,
+  /* Many rows per expert, producer/consumer form ([release] performance
+   * highlights: a persistent main loop whose loads and dequantisation run
+   * in dedicated warps beside the matrix operations): a persistent grid
+   * of one workgroup per compute unit in which producer waves stage token
+   * rows and dequantised weights in LDS and consumer waves only run MFMAs.
+   * Same 128 x 256 blocks and bit-identical results as
+   * QMA_KERNEL_LARGE_M; no split-K. Never chosen by the planner (it runs
+   * slower than QMA_KERNEL_LARGE_M on gfx950); a caller selects it by
+   * setting plan.kernel. */
+  QMA_KERNEL_LARGE_M_PC = 3
 } qma_kernel;
 
 /* A plan: a pure function of the layer's shape and the host-known token
@@ -106,7 +117,8 @@ typedef enum qma_kernel {
  * QMA_ERR_INVALID_ARG and before any launch, a plan made for another layer
  * or one that names no compiled kernel instance (small-M: block_m in
  * {16, 32, 64}, waves_k in {1, 2, 4}, at most 8 16x16 tiles per wave;
- * large-M: a 128 x 256 block), or whose split_k is outside [1, 8] or above
+ * large-M: a 128 x 256 block, and split_k = 1 for the producer/consumer
+ * form), or whose split_k is outside [1, 8] or above
  * K/128 (every K partition owns at least one 128-wide chunk). k_depth
  * outside an instance's supported depths falls back to that instance's
  * default. */

@@ -226,11 +226,14 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
   if (plan->path != L.path || plan->n != L.N || plan->k != L.K ||
       plan->num_experts != L.E)
     return fail(QMA_ERR_INVALID_ARG, "plan was made for another layer");
-  if (plan->kernel != QMA_KERNEL_SMALL_M && plan->kernel != QMA_KERNEL_LARGE_M)
+  if (plan->kernel != QMA_KERNEL_SMALL_M && plan->kernel != QMA_KERNEL_LARGE_M &&
+      plan->kernel != QMA_KERNEL_LARGE_M_PC)
     return fail(QMA_ERR_INVALID_ARG, "plan has unknown kernel %d", plan->kernel);
-  if (plan->kernel == QMA_KERNEL_LARGE_M &&
-      (plan->block_m != 128 || plan->block_n != 256 || L.N % 256 != 0))
+  const bool large = plan->kernel != QMA_KERNEL_SMALL_M;
+  if (large && (plan->block_m != 128 || plan->block_n != 256 || L.N % 256 != 0))
     return fail(QMA_ERR_INVALID_ARG, "large-M plan needs block 128 x 256 and N %% 256 == 0");
+  if (plan->kernel == QMA_KERNEL_LARGE_M_PC && plan->split_k != 1)
+    return fail(QMA_ERR_INVALID_ARG, "the producer/consumer large-M kernel takes no split-K");
   if (plan->block_m < 16 || plan->block_m % 16 != 0 ||
       (plan->kernel == QMA_KERNEL_SMALL_M && plan->block_m > 64))
     return fail(QMA_ERR_INVALID_ARG, "plan has bad block_m %d", plan->block_m);

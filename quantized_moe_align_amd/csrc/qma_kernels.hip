@@ -1462,6 +1462,470 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
   }
 }
 
+// ---------------------------------------------------------------------------
+// Large-M expert GEMM, producer/consumer form (prefill and contiguous shapes;
+// [release] performance highlights: the grouped kernels run a persistent main
+// loop in which some warps load and dequantise while others run the matrix
+// operations).
+//
+// One workgroup per CU with 16 waves: 8 consumers and 8 producers (two of
+// each per SIMD). The grid is persistent. Workgroup (x = id % 8,
+// slot = id / 8) walks the items (128-row tile, 256-column block) of the
+// tiles dealt to XCD x (tiles x, x + 8, ...), taking every (G/8)-th item, so
+// a tile's column blocks run on one XCD and share its token rows in that
+// L2. The items of a workgroup form one stream of 64-wide K stages.
+//
+// Producers. Producer w owns 32-column tile w of the block and one 16-wide K
+// step (w % 2) of 32 token rows (w / 2). Stages are 32 wide in K. Per stage
+// a producer copies its token rows of the stage four ahead into LDS with a
+// direct-to-LDS load (rows with no token arrive as zeros without being
+// read), keeps its packed weights in registers up to eight stages ahead
+// (three 128-wide chunks in flight), and dequantises the current stage's
+// quarter chunk into LDS once for the whole workgroup, as bf16((q - 8) s)
+// (the same rounding as the kernel above) laid
+// out as 32 x 32 x 16 MFMA B fragments: for 32-column tile ct and K step ks,
+// lane l's 16 bytes hold column 32 ct + l % 32, K rows 16 ks + 8 (l / 32)
+// .. +7, which is exactly one packed word.
+//
+// Consumers. Read A fragments (token rows stored K-step-major, 32 bytes per
+// row and K step, the two 16-byte halves swapped on rows whose bit 3 is set,
+// so that the 16 lanes the LDS serves together hit distinct banks) and B
+// fragments from LDS, and issue v_mfma_f32_32x32x16_bf16 only. With three
+// or four occupied 32-row groups the eight consumers split the tile two
+// (row halves) by four (64-column quarters); with one or two, eight ways by
+// 32 columns.
+//
+// Hand-over. No workgroup barrier in the main loop: a producer bumps
+// full[s % 5] once its part of stage s has landed (its own direct-to-LDS
+// load waited by count, its LDS writes waited), and a consumer bumps
+// released[s % 5] once its reads of stage s have returned. Nine token-row
+// buffers and five weight buffers: producers may run four stages ahead of
+// the consumers, and token rows load four stages ahead of the
+// dequantisation, across item boundaries, so the next item's first stages
+// load while consumers store the current one; both buffers a producer
+// refills at stage t were last used by stage t - 5. Row tables (output row
+// per tile row, occupied groups) rotate over three slots, one per item in
+// flight. Every wait is bounded: past its budget a wave stops waiting, so a
+// fault in the hand-over would show as wrong output, never as a hang.
+// Outputs are stored straight from the accumulators, two columns per lane
+// (adjacent lanes swap values so that each stores 4 bytes of one row).
+// ---------------------------------------------------------------------------
+constexpr int kPcLead = 4;                        // stages producers may run ahead
+constexpr int kPcAhead = 4;                       // token rows load this many stages ahead
+constexpr int kPcNB = kPcLead + 1;                // dequantised-weight stage buffers
+constexpr int kPcNA = kPcAhead + kPcLead + 1;     // token-row stage buffers
+constexpr int kPcTabs = 3;                        // row-table slots (items in flight)
+constexpr int kPcSK = 32;                         // K elements per stage
+constexpr int kPcKS = kPcSK / 16;                 // 16-wide K steps per stage
+constexpr int kPcQ = kChunkK / kPcSK;             // stages per 128-wide packed chunk
+constexpr int kPcProd = 8;                        // producer waves
+constexpr int kPcCons = 8;                        // consumer waves
+constexpr int kPcThreads = 64 * (kPcProd + kPcCons);
+constexpr int kPcRowBytes = kPcSK * 2;            // a token row's stage: 64 B
+constexpr int kPcAStep = kLmBM * 32;              // one K step of the tile: 4 KiB
+constexpr int kPcAStage = kPcKS * kPcAStep;       // 8 KiB: [2 K steps][128 rows][32 B]
+constexpr int kPcBStep = 64 * 16;                 // one B fragment: 1 KiB
+constexpr int kPcBTile = kPcKS * kPcBStep;        // a 32-column tile's stage: 2 KiB
+constexpr int kPcBStage = (kLmBN / 32) * kPcBTile; // 16 KiB
+constexpr int kPcSpinBudget = 1 << 24;            // sleeps per wave (s_sleep 1: ~64 cycles)
+
+// Loads each producer issues per stage: one direct-to-LDS row load (for the
+// stage kPcAhead ahead), and on the first stage of each chunk the weights of
+// the chunk two ahead (two weight and two scale loads). At the signal of
+// stage t the loads issued after A(t) are the next kPcAhead row loads and
+// the chunks issued at stages t - kPcAhead .. t: two when t starts a chunk,
+// else one.
+constexpr int kPcALoads = 1;
+constexpr int kPcWLoads = 4;
+constexpr int kPcSigWait0 = kPcAhead * kPcALoads + 2 * kPcWLoads;       // 12
+constexpr int kPcSigWait = kPcAhead * kPcALoads + kPcWLoads;            // 8
+// Loads issued after W(c) when stage kPcQ c dequantises it: eight row loads
+// and two chunks in steady state; fewer for chunks 0 and 1 (the prologue
+// issues them with fewer loads behind them).
+constexpr int kPcDeqWait = 2 * kPcQ * kPcALoads + 2 * kPcWLoads;         // 16
+constexpr int kPcDeqWait0 = kPcALoads + 2 * kPcWLoads;                   // 9
+constexpr int kPcDeqWait1 = (kPcQ + 1) * kPcALoads + 2 * kPcWLoads;      // 13
+
+__device__ __forceinline__ void wait_lgkm0() {
+  // s_waitcnt lgkmcnt(0), vector-memory and export counts unconstrained
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4));
+}
+
+// The hand-over counters are read and bumped with inline-asm LDS operations
+// (the read waits for itself in the same asm block). As compiler-visible
+// LDS accesses they would be ordered behind every outstanding direct-to-LDS
+// load (the compiler cannot tell the counters from the load destinations)
+// and drain the producers' prefetch queue at every stage. `budget` is the
+// wave's remaining sleeps over the whole kernel: once spent, waits return
+// at once, so a broken hand-over ends the kernel in about a second instead
+// of hanging it.
+__device__ __forceinline__ void pc_wait(const int32_t* flag, int target, int& budget) {
+  const uint32_t addr = lds_addr(flag);
+  for (;;) {
+    int v;
+    asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+    if (__builtin_amdgcn_readfirstlane(v) >= target || budget <= 0) break;
+    --budget;
+    __builtin_amdgcn_s_sleep(1);
+  }
+  asm volatile("" ::: "memory");
+}
+
+// One increment per wave; the caller has waited for the data it publishes.
+__device__ __forceinline__ void pc_signal(int32_t* flag, int lane) {
+  const uint32_t addr = lds_addr(flag);
+  const int one = 1;
+  asm volatile("" ::: "memory");
+  if (lane == 0) asm volatile("ds_add_u32 %0, %1" : : "v"(addr), "v"(one) : "memory");
+  asm volatile("" ::: "memory");
+}
+
+// Items of one workgroup: tiles x, x + 8, ... of the routed tiles, each
+// with its column blocks, every GX-th item from `slot`.
+struct PcWalk {
+  int x, slot, GX, n_my, nblocks;
+  __device__ __forceinline__ void item(const GemmParams& p, int i, int& tile, int& nb,
+                                       int& e) const {
+    const int q = slot + i * GX;
+    const int j = q / nblocks;
+    nb = q - j * nblocks;
+    tile = x + 8 * j;
+    e = tile_expert(p, tile);
+  }
+};
+
+__device__ __forceinline__ PcWalk pc_walk(const GemmParams& p) {
+  PcWalk w;
+  const int G = (int)gridDim.x;
+  w.x = (int)blockIdx.x & 7;
+  w.slot = (int)blockIdx.x >> 3;
+  w.GX = G >> 3;
+  w.nblocks = p.nblocks;
+  const int ntiles = p.mode == 0 ? min(*p.ntp / p.BM, p.num_tiles) : p.num_tiles;
+  const int nt_x = ntiles > w.x ? (ntiles - w.x + 7) / 8 : 0;
+  const int nq = nt_x * p.nblocks;
+  w.n_my = nq > w.slot ? (nq - w.slot + w.GX - 1) / w.GX : 0;
+  return w;
+}
+
+struct PcLds {
+  uint8_t* a;          // [kPcNA][kPcAStage]
+  uint8_t* b;          // [kPcNB][kPcBStage]
+  int32_t* out;        // [kPcTabs][kLmBM] output row per tile row (-1: none)
+  int32_t* gv;         // [kPcTabs][4] 32-row group holds a token
+  int32_t* full;       // [kPcNB] producers done with the stage
+  int32_t* released;   // [kPcNB] consumers done with the stage
+  int32_t* done;       // items whose outputs every consumer has stored
+};
+
+// 16-byte half h of row r's 32 bytes of a K step sits at half h ^ (bit 3 of r)
+__device__ __forceinline__ int pc_half(int row, int h) { return h ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ void pc_producer(const GemmParams& p, const PcWalk& wk, const PcLds& s, int pw,
+                            int lane) {
+  const int KC = p.KC, KS = kPcQ * KC;
+  const int S = wk.n_my * KS;                      // stages of this workgroup
+  const int U = wk.n_my * KC;                      // chunks
+  const uint32_t tile_bytes = (uint32_t)KC * kWBlockBytes;
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(uniform_ptr(p.a), p.a_bytes);
+  const int c16 = lane & 15;
+  const int aks = pw & 1;                          // this producer's K step of token rows
+  const int arow0 = (pw >> 1) * 32;                // and its 32 rows
+  int budget = kPcSpinBudget;
+
+  // token rows of the item the row loads are on
+  uint32_t voff_a[kPcALoads];
+  auto enter_item = [&](int i) __attribute__((always_inline)) {
+    int tile, nb, e;
+    wk.item(p, i, tile, nb, e);
+    const int tslot = i % kPcTabs;
+    // the row table slot was last read by the epilogue of item i - kPcTabs
+    if (i >= kPcTabs) pc_wait(s.done, (i - kPcTabs + 1) * kPcCons, budget);
+    const int row = arow0 + (lane & 31);
+    RowInfo ri = row_info(p, tile, e, row);
+    ri.valid = ri.valid && e >= 0;
+    if (aks == 0) {
+      if (lane < 32) s.out[tslot * kLmBM + row] = ri.valid ? ri.out_row : -1;
+      const uint64_t any = __ballot(lane < 32 && ri.valid);
+      if (lane == 0) s.gv[tslot * 4 + (pw >> 1)] = any != 0 ? 1 : 0;
+    }
+    // lane L: row arow0 + L/2, LDS half L % 2, which holds K half
+    // (L % 2) ^ (bit 3 of the row) of K step aks
+    const int ar = __shfl(ri.valid ? ri.a_row : -1, lane >> 1, 64);
+    const int kh = pc_half(lane >> 1, lane & 1);
+    voff_a[0] = ar >= 0 ? (uint32_t)ar * (uint32_t)p.K * 2u + (uint32_t)(aks * 32 + kh * 16)
+                        : 0x80000000u;
+  };
+  // direct-to-LDS loads of stage t's token rows (past the end: the last
+  // stage again, into a buffer no consumer reads afterwards)
+  auto load_a = [&](int t) __attribute__((always_inline)) {
+    const int tt = min(t, S - 1);
+    const int i = tt / KS, st = tt - i * KS;
+    if (st == 0 && t < S) enter_item(i);
+    uint8_t* dst = s.a + (t % kPcNA) * kPcAStage + aks * kPcAStep + arow0 * 32;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (__attribute__((address_space(3))) void*)dst, 16,
+                                             (int)voff_a[0], st * kPcRowBytes, 0, 0);
+  };
+
+  // weights: ring of three chunks of this producer's two 16-column tiles
+  u32x4 wv[3][2];
+  u32x2 sv[3][2];
+  int w_item = -1;
+  const uint8_t* wbase = p.wpk;
+  const uint8_t* sbase = p.spk;
+  auto load_w = [&](auto ring_c, int u) __attribute__((always_inline)) {
+    constexpr int r = decltype(ring_c)::value;
+    u = min(u, U - 1);
+    const int i = u / KC, c = u - i * KC;
+    if (i != w_item) {
+      int tile, nb, e;
+      wk.item(p, i, tile, nb, e);
+      const size_t t0 = (size_t)max(e, 0) * p.NT + (size_t)nb * (kLmBN / 16) + pw * 2;
+      wbase = p.wpk + t0 * tile_bytes;
+      sbase = p.spk + t0 * (size_t)KC * kSBlockBytes;
+      w_item = i;
+    }
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(uniform_ptr(wbase), 2 * tile_bytes);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(uniform_ptr(sbase), 2 * (uint32_t)KC * kSBlockBytes);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      wv[r][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, t * tile_bytes + c * kWBlockBytes,
+                                                       kNonTemporal);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+      sv[r][t] = __builtin_amdgcn_raw_buffer_load_b64(rs, c16 * 8, (t * KC + c) * kSBlockBytes, 0);
+  };
+  // dequantise quarter j (word j, scale group j) of the chunk in ring slot
+  // r into weight buffer b: this producer's 32-column tile ct = pw, K step
+  // lane / 32 of the stage
+  const uint32_t bdst0 = (uint32_t)(pw * kPcBTile) +
+                         (uint32_t)((c16 + 32 * ((lane >> 4) & 1)) * 16 + (lane >> 5) * kPcBStep);
+  auto dequant = [&](auto ring_c, auto j_c, int b) __attribute__((always_inline)) {
+    constexpr int r = decltype(ring_c)::value;
+    constexpr int j = decltype(j_c)::value;
+    uint8_t* dst = s.b + b * kPcBStage + bdst0;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const uint32_t sw = sv[r][t][j >> 1];      // scales of groups 2 (j/2), +1
+      const float sc = (j & 1) ? bf16_hi(sw) : bf16_lo(sw);
+      const u32x4 v = dequant8(wv[r][t][j], sc, -8.0f * sc);
+      *(u32x4*)(dst + t * 256) = v;
+    }
+  };
+
+  if (S == 0) return;
+  // Prologue: the token rows of the first kPcAhead stages (with item 0's
+  // row table), then two weight chunks.
+#pragma unroll
+  for (int t = 0; t < kPcAhead; ++t) load_a(t);
+  load_w(std::integral_constant<int, 0>{}, 0);
+  load_w(std::integral_constant<int, 1>{}, 1);
+
+  // Step t: [stage t - kPcNB released: both buffers refilled below are
+  // free] A(t + kPcAhead) [W(t/4 + 2) when t starts a chunk] [W(t/4) has
+  // landed] dequantise B(t) [A(t) has landed] signal full(t). Steps are
+  // unrolled in groups of 12 (three chunks), so the register ring slot of
+  // every chunk is a constant.
+  auto step = [&](int t, auto k_c, auto deq_wait_c) __attribute__((always_inline)) {
+    constexpr int k = decltype(k_c)::value;          // t % 12
+    constexpr int deq_wait = decltype(deq_wait_c)::value;
+    constexpr int ring = k / kPcQ;                   // chunk t/4 lives in ring (t/4) % 3
+    if (t >= kPcNB) pc_wait(&s.released[t % kPcNB], (t / kPcNB) * kPcCons, budget);
+    load_a(t + kPcAhead);
+    if constexpr (k % kPcQ == 0) {
+      load_w(std::integral_constant<int, (ring + 2) % 3>{}, t / kPcQ + 2);
+      wait_vmcnt<deq_wait>();
+    }
+    dequant(std::integral_constant<int, ring>{}, std::integral_constant<int, k % kPcQ>{},
+            t % kPcNB);
+    wait_vmcnt<(k % kPcQ == 0) ? kPcSigWait0 : kPcSigWait>();
+    wait_lgkm0();
+    pc_signal(&s.full[t % kPcNB], lane);
+  };
+  auto group = [&](int t0, auto first_c) __attribute__((always_inline)) {
+    constexpr bool first = decltype(first_c)::value;
+    using WS = std::integral_constant<int, kPcDeqWait>;
+    static_for<12>([&](auto k_c) __attribute__((always_inline)) {
+      constexpr int k = decltype(k_c)::value;
+      constexpr int dw = !first ? kPcDeqWait : (k == 0 ? kPcDeqWait0 : (k == 4 ? kPcDeqWait1 : kPcDeqWait));
+      if (t0 + k < S) step(t0 + k, k_c, std::integral_constant<int, dw>{});
+      __builtin_amdgcn_sched_barrier(0);
+      (void)WS{};
+    });
+  };
+  group(0, std::true_type{});
+  for (int t0 = 12; t0 < S; t0 += 12) group(t0, std::false_type{});
+  // every direct-to-LDS load has landed before the workgroup can end
+  wait_vmcnt<0>();
+}
+
+template <int NV, int NT>
+__device__ __forceinline__ void pc_store(const GemmParams& p, const int32_t* out_rows, int nb,
+                                         int gr0, int ct0, int lane, const f32x16 (&acc)[2][2]) {
+  const int l32 = lane & 31, kq = lane >> 5;
+  const bool odd = lane & 1;
+#pragma unroll
+  for (int m = 0; m < NV; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // output rows of accumulator elements 4i .. 4i+3: rows R0 .. R0+3
+      const int R0 = (gr0 + m) * 32 + 8 * i + 4 * kq;
+      const int4 orow4 = *(const int4*)(out_rows + R0);
+      const int ov[4] = {orow4.x, orow4.y, orow4.z, orow4.w};
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int r = 0; r < 4; r += 2) {
+          const int C = (ct0 + n) * 32 + l32;                   // column in the block
+          float x0 = acc[m][n][4 * i + r], x1 = acc[m][n][4 * i + r + 1];
+          const int o0 = ov[r], o1 = ov[r + 1];
+          if (p.mode == 0 && p.topk_w) {
+            x0 *= o0 >= 0 ? p.topk_w[o0] : 1.0f;
+            x1 *= o1 >= 0 ? p.topk_w[o1] : 1.0f;
+          }
+          // even lane stores (R; C, C+1), odd lane (R+1; C-1, C)
+          const float send = odd ? x0 : x1;
+          const float recv = __int_as_float(
+              __builtin_amdgcn_mov_dpp(__float_as_int(send), 0xB1, 0xF, 0xF, false));
+          const float lo = odd ? recv : x0, hi = odd ? x1 : recv;
+          const int orow = odd ? o1 : o0;
+          const int col = nb * kLmBN + (odd ? C - 1 : C);
+          const uint32_t v = cvt_pk_bf16(lo, hi);
+          if (orow >= 0) *(uint32_t*)(p.c + (size_t)orow * p.N + col) = v;
+        }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// All stages of one item and its stores, for a consumer whose tile is NV
+// 32-row groups from gr0 by NT 32-column tiles from ct0 (NV = 0: the item
+// has no token; stages are only waited for and released). t is the
+// workgroup's stage counter at the item's first stage. Fragment reads run
+// one K step ahead of the MFMAs, also across stages: stage t is released
+// as soon as its reads have returned, and before its last K step's MFMAs
+// the consumer waits for stage t + 1 and reads its first fragments, so both
+// latencies hide behind MFMAs already issued.
+template <int NV, int NT>
+__device__ __forceinline__ void pc_consume_item(const GemmParams& p, const PcLds& s, int lane,
+                                                int t, int KS, int nb, int gr0, int ct0,
+                                                const int32_t* orows, int& budget) {
+  if constexpr (NV == 0) {
+    for (int st = 0; st < KS; ++st, ++t) {
+      pc_wait(&s.full[t % kPcNB], (t / kPcNB + 1) * kPcProd, budget);
+      pc_signal(&s.released[t % kPcNB], lane);
+    }
+  } else {
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) acc[m][n] = f32x16{};
+    // lane's A fragment: row gr0*32 + lane % 32, K half lane / 32 of the K
+    // step; B fragment: tile ct0, lane's 16 bytes. Every other fragment is at
+    // a constant offset from these.
+    const int arow = gr0 * 32 + (lane & 31);
+    const uint8_t* a0 = s.a + arow * 32 + pc_half(arow, lane >> 5) * 16;
+    const uint8_t* b0 = s.b + ct0 * kPcBTile + lane * 16;
+    u32x4 av[2][NV], bv[2][NT];
+    auto rd = [&](int slot, int tt, int ks) __attribute__((always_inline)) {
+      const uint8_t* ab = a0 + (tt % kPcNA) * kPcAStage + ks * kPcAStep;
+      const uint8_t* bb = b0 + (tt % kPcNB) * kPcBStage + ks * kPcBStep;
+#pragma unroll
+      for (int m = 0; m < NV; ++m) av[slot][m] = *(const u32x4*)(ab + m * 32 * 32);
+#pragma unroll
+      for (int n = 0; n < NT; ++n) bv[slot][n] = *(const u32x4*)(bb + n * kPcBTile);
+    };
+    auto mma = [&](int slot) __attribute__((always_inline)) {
+#pragma unroll
+      for (int m = 0; m < NV; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] = mfma32(av[slot][m], bv[slot][n], acc[m][n]);
+    };
+    pc_wait(&s.full[t % kPcNB], (t / kPcNB + 1) * kPcProd, budget);
+    rd(0, t, 0);
+    for (int st = 0; st < KS; ++st, ++t) {
+      rd(1, t, 1);
+      mma(0);
+      // the reads of stage t have returned once the last one has
+      wait_lgkm0();
+      pc_signal(&s.released[t % kPcNB], lane);
+      if (st + 1 < KS) {
+        pc_wait(&s.full[(t + 1) % kPcNB], ((t + 1) / kPcNB + 1) * kPcProd, budget);
+        rd(0, t + 1, 0);
+      }
+      mma(1);
+    }
+    pc_store<NV, NT>(p, orows, nb, gr0, ct0, lane, acc);
+  }
+}
+
+__device__ __forceinline__ void pc_consumer(const GemmParams& p, const PcWalk& wk, const PcLds& s, int cw,
+                            int lane) {
+  const int KS = kPcQ * p.KC;
+  int budget = kPcSpinBudget;
+  for (int i = 0, t = 0; i < wk.n_my; ++i, t += KS) {
+    int tile, nb, e;
+    wk.item(p, i, tile, nb, e);
+    const int tslot = i % kPcTabs;
+    // the item's row table is published with its first stage
+    pc_wait(&s.full[t % kPcNB], (t / kPcNB + 1) * kPcProd, budget);
+    const int* gv = s.gv + tslot * 4;
+    // occupied 32-row groups: one past the last group holding a token
+    const int g = __builtin_amdgcn_readfirstlane(gv[3] ? 4 : gv[2] ? 3 : gv[1] ? 2 : gv[0] ? 1 : 0);
+    const int32_t* orows = s.out + tslot * kLmBM;
+    if (g >= 3) {
+      // two row halves x four 64-column quarters
+      const int gr0 = 2 * (cw >> 2), ct0 = 2 * (cw & 3);
+      if (g - gr0 >= 2)
+        pc_consume_item<2, 2>(p, s, lane, t, KS, nb, gr0, ct0, orows, budget);
+      else
+        pc_consume_item<1, 2>(p, s, lane, t, KS, nb, gr0, ct0, orows, budget);
+    } else if (g == 2) {
+      // eight 32-column slices over both groups
+      pc_consume_item<2, 1>(p, s, lane, t, KS, nb, 0, cw, orows, budget);
+    } else if (g == 1) {
+      pc_consume_item<1, 1>(p, s, lane, t, KS, nb, 0, cw, orows, budget);
+    } else {
+      pc_consume_item<0, 1>(p, s, lane, t, KS, nb, 0, 0, orows, budget);
+    }
+    // this consumer no longer reads item i's row table
+    wait_lgkm0();
+    pc_signal(s.done, lane);
+  }
+}
+
+__global__ __launch_bounds__(kPcThreads, 1) void gemm_large_m_pc_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_a[kPcNA * kPcAStage];
+  __shared__ __attribute__((aligned(1024))) uint8_t s_b[kPcNB * kPcBStage];
+  __shared__ __attribute__((aligned(16))) int32_t s_out[kPcTabs * kLmBM];
+  __shared__ int32_t s_gv[kPcTabs * 4];
+  __shared__ int32_t s_full[kPcNB];
+  __shared__ int32_t s_released[kPcNB];
+  __shared__ int32_t s_done;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  if (threadIdx.x < kPcNB) {
+    s_full[threadIdx.x] = 0;
+    s_released[threadIdx.x] = 0;
+  }
+  if (threadIdx.x == 0) s_done = 0;
+  __syncthreads();
+  const PcWalk wk = pc_walk(p);
+  if (wk.n_my == 0) return;
+  // (an offset the compiler cannot fold keeps this a run-time value: as a
+  // constant it would become a global whose initializer holds LDS
+  // addresses, which the target cannot emit)
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  const PcLds s{s_a + z, s_b + z, s_out + z, s_gv + z, s_full + z, s_released + z, &s_done + z};
+  // waves 0..7 consume, 8..15 produce: each SIMD holds two of each
+  if (w >= kPcCons)
+    pc_producer(p, wk, s, w - kPcCons, lane);
+  else
+    pc_consumer(p, wk, s, w, lane);
+}
+
 template <int TM, int NTW, int WK, int D>
 static int launch_small_m_inst(const GemmParams& gp, unsigned grid, hipStream_t st) {
   hipLaunchKernelGGL((gemm_small_m_kernel<TM, NTW, WK, D>), dim3(grid), dim3(256), 0, st, gp);
@@ -1525,6 +1989,14 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int64_t grid = tiles_pad * gp.nblocks * gp.split;
   if (grid <= 0) return 0;
   if (grid >= (1ll << 24)) return (int)hipErrorInvalidConfiguration;
+  if (pl.kernel == QMA_KERNEL_LARGE_M_PC) {
+    if (pl.block_m != kLmBM || pl.block_n != kLmBN || L.N % kLmBN != 0 || gp.split != 1)
+      return (int)hipErrorInvalidConfiguration;
+    // persistent: one workgroup per CU, a multiple of the 8 XCDs
+    hipLaunchKernelGGL(gemm_large_m_pc_kernel, dim3((unsigned)kNumCUs), dim3(kPcThreads), 0, st,
+                       gp);
+    return (int)hipGetLastError();
+  }
   if (pl.kernel == QMA_KERNEL_LARGE_M) {
     if (pl.block_m != kLmBM || pl.block_n != kLmBN || L.N % kLmBN != 0)
       return (int)hipErrorInvalidConfiguration;

@@ -22,7 +22,8 @@ QMA_OK, QMA_ERR_INVALID_ARG, QMA_ERR_UNSUPPORTED, QMA_ERR_ROUTING, \
 PATH_INDEXED, PATH_GROUPED_CONTIGUOUS, PATH_GROUPED_MASKED = 0, 1, 2
 DTYPE_BF16, DTYPE_FP16, DTYPE_FP32 = 1, 2, 3
 PACK_INT32_K8 = 1
-KERNEL_SMALL_M, KERNEL_LARGE_M = 1, 2
+KERNEL_SMALL_M, KERNEL_LARGE_M, KERNEL_LARGE_M_PC = 1, 2, 3
+LARGE_M_KERNELS = (KERNEL_LARGE_M, KERNEL_LARGE_M_PC)
 PROFILES = {0: "generic", 1: "ep_gate_up", 2: "ep_down", 3: "tp_gate_up", 4: "tp_down"}
 
 # Every symbol include/qma.h declares.

@@ -246,7 +246,8 @@ def test_contiguous(gpu, integer):
     a_poison[m_idx < 0] = 0x7FC0                             # padding rows are never read
     for override in (None, {"kernel": 1, "block_m": 16, "block_n": 64, "waves_k": 4},
                      {"kernel": 1, "block_m": 32, "block_n": 128, "waves_k": 2},
-                     {"split_k": 2}):
+                     {"kernel": qma.KERNEL_LARGE_M, "split_k": 2},
+                     {"kernel": qma.KERNEL_LARGE_M, "split_k": 1}):
         got = contiguous(a_poison, m_idx, w, s, override)
         ref = O.grouped_contiguous(a, m_idx, w, s)
         valid = m_idx >= 0
@@ -299,7 +300,7 @@ def test_indexed_equals_contiguous_on_same_rows(gpu):
     assert np.array_equal(got_c[valid], got_i[valid])
     got_cl = contiguous(wl["a"], m_idx, w, s, {"split_k": 1})          # large-M
     got_il, pl = indexed(wl["a"], 1, ids, w, s, force_bm=128, override={"split_k": 1})
-    assert pl.kernel == qma.KERNEL_LARGE_M
+    assert pl.kernel in qma.LARGE_M_KERNELS
     assert_per_expert(got_cl, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx)
     assert np.array_equal(got_cl[valid], got_il[valid])
 
@@ -318,24 +319,33 @@ HALF_TILE_COUNTS = [1, 31, 32, 33, 63, 64, 65, 95, 96, 97, 127, 128, 129, 191, 1
                     0, 256, 287]
 
 
-@pytest.mark.parametrize("split", [1, 2])
-def test_large_m_half_tiles_bitwise(gpu, split):
+# the two large-M kernels: (kernel, split_k)
+LM_VARIANTS = [(qma.KERNEL_LARGE_M, 1), (qma.KERNEL_LARGE_M, 2), (qma.KERNEL_LARGE_M_PC, 1)]
+LM_IDS = ["large_m", "large_m_split2", "large_m_pc"]
+
+
+@pytest.mark.parametrize("kernel,split", LM_VARIANTS, ids=LM_IDS)
+def test_large_m_half_tiles_bitwise(gpu, kernel, split):
     E, K, N = len(HALF_TILE_COUNTS), 512, 256
     rng = np.random.default_rng(70 + split)
     w, s = weights(rng, E, N, K, integer=True)
     ids = np.repeat(np.arange(E, dtype=np.int32), HALF_TILE_COUNTS)
     ids = rng.permutation(ids)[:, None]
     a = bf16_small_ints(rng, (ids.shape[0], K))
-    got, plan = indexed(a, 1, ids, w, s, force_bm=128, override={"split_k": split})
-    assert plan.kernel == qma.KERNEL_LARGE_M and plan.split_k == split
+    got, plan = indexed(a, 1, ids, w, s, force_bm=128,
+                        override={"kernel": kernel, "split_k": split})
+    assert plan.kernel == kernel and plan.split_k == split
     ref = O.moe_gemm_by_slot(a, 1, ids, w, s)
     assert np.array_equal(got, rne(ref))
 
 
-def test_large_m_several_rounds_per_xcd_bitwise(gpu):
+@pytest.mark.parametrize("kernel", [qma.KERNEL_LARGE_M, qma.KERNEL_LARGE_M_PC],
+                         ids=["large_m", "large_m_pc"])
+def test_large_m_several_rounds_per_xcd_bitwise(gpu, kernel):
     # 45 tiles dealt to the 8 XCDs (5 or 6 each) x 16 column blocks: each
-    # XCD's list spans more than one round of its workgroup slots, and the
-    # ragged experts' last tiles are partly filled
+    # XCD's list spans more than one round of its workgroup slots (several
+    # items per persistent workgroup), and the ragged experts' last tiles are
+    # partly filled
     K, N = 256, 4096
     counts = [2200, 1300, 900, 700, 33, 3]
     E = len(counts)
@@ -343,20 +353,20 @@ def test_large_m_several_rounds_per_xcd_bitwise(gpu):
     w, s = weights(rng, E, N, K, integer=True)
     ids = rng.permutation(np.repeat(np.arange(E, dtype=np.int32), counts))[:, None]
     a = bf16_small_ints(rng, (ids.shape[0], K))
-    got, plan = indexed(a, 1, ids, w, s, force_bm=128, override={"split_k": 1})
-    assert plan.kernel == qma.KERNEL_LARGE_M and plan.block_n == 256
+    got, plan = indexed(a, 1, ids, w, s, force_bm=128, override={"split_k": 1, "kernel": kernel})
+    assert plan.kernel == kernel and plan.block_n == 256
     ref = O.moe_gemm_by_slot(a, 1, ids, w, s)
     assert np.array_equal(got, rne(ref))
 
 
-@pytest.mark.parametrize("split", [1, 2])
-def test_large_m_masked_half_tiles_bitwise(gpu, split):
+@pytest.mark.parametrize("kernel,split", LM_VARIANTS, ids=LM_IDS)
+def test_large_m_masked_half_tiles_bitwise(gpu, kernel, split):
     E, Mb, K, N = 11, 256, 256, 256
     rng = np.random.default_rng(80 + split)
     masked_m = np.array([0, 1, 31, 33, 64, 65, 96, 97, 129, 161, 256], np.int32)
     w, s = weights(rng, E, N, K, integer=True)
     a = bf16_small_ints(rng, (E, Mb, K))
-    large = {"kernel": qma.KERNEL_LARGE_M, "block_m": 128, "block_n": 256, "waves_k": 1,
+    large = {"kernel": kernel, "block_m": 128, "block_n": 256, "waves_k": 1,
              "split_k": split}
     got = masked(a, masked_m, 128, w, s, large)
     ref = O.grouped_masked(a, masked_m, w, s)
@@ -373,14 +383,19 @@ def test_large_m_integer_exact_bitwise(gpu, shape):
     w, s = weights(rng, E, N, K, integer=True)
     a = bf16_small_ints(rng, (T, K))
     ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
-    got, plan = indexed(a, topk, ids, w, s)
+    planned, plan = indexed(a, topk, ids, w, s)
     assert plan.kernel == qma.KERNEL_LARGE_M and plan.block_m == 128
+    got, _ = indexed(a, topk, ids, w, s,
+                     override={"kernel": qma.KERNEL_LARGE_M_PC, "split_k": 1})
     ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
     valid = slot_experts(ids, E) >= 0
     assert np.array_equal(got[valid], rne(ref[valid]))
     assert np.all(got[~valid] == SENT)
-    split, _ = indexed(a, topk, ids, w, s, override={"split_k": 2})
+    assert np.array_equal(planned, got)
+    split, _ = indexed(a, topk, ids, w, s, override={"split_k": 2, "kernel": qma.KERNEL_LARGE_M})
     assert np.array_equal(split, got)
+    one, _ = indexed(a, topk, ids, w, s, override={"kernel": qma.KERNEL_LARGE_M, "split_k": 1})
+    assert np.array_equal(one, got)
 
 
 @pytest.mark.parametrize("shape", LARGE_SHAPES)
@@ -391,10 +406,14 @@ def test_large_m_random_within_tolerance(gpu, shape):
     a = inputs.bf16_normal(rng, (T, K))
     ids = rng.integers(0, E, (T, topk)).astype(np.int32)
     tw = rng.random(T * topk).astype(np.float32)
-    got, plan = indexed(a, topk, ids, w, s, topk_w=tw)
-    assert plan.kernel == qma.KERNEL_LARGE_M
+    got, plan = indexed(a, topk, ids, w, s, topk_w=tw,
+                        override={"kernel": qma.KERNEL_LARGE_M_PC, "split_k": 1})
     ref = O.moe_gemm_by_slot(a, topk, ids, w, s, topk_weights=tw)
     assert_per_expert(got, ref, slot_experts(ids, E), f"large-M {shape}")
+    # the two large-M kernels sum the same products in the same K order
+    old, _ = indexed(a, topk, ids, w, s, topk_w=tw,
+                     override={"kernel": qma.KERNEL_LARGE_M, "split_k": 1})
+    assert np.array_equal(old, got)
 
 
 def test_large_m_nan_poisoned_padding(gpu):
@@ -407,7 +426,7 @@ def test_large_m_nan_poisoned_padding(gpu):
     s_p = s.copy(); s_p[3] = 0x7FC0
     a_p = a.copy(); a_p[:7] = 0x7FC0
     got, plan = indexed(a_p, topk, ids, w, s_p, force_bm=128)
-    assert plan.kernel == qma.KERNEL_LARGE_M
+    assert plan.kernel in qma.LARGE_M_KERNELS
     assert_per_expert(got, O.moe_gemm_by_slot(a, topk, ids, w, s), slot_experts(ids, E))
 
 
@@ -473,7 +492,8 @@ def test_graph_capture_large_m_split_k(gpu):
     w13, s13 = weights(rng, E, 2 * I, K)
     w2, s2 = weights(rng, E, K, I)
     moe = IndexedMoE(ExpertWeights(w13, s13), ExpertWeights(w2, s2), T, 1, force_block_m=128)
-    assert moe.plan13.kernel == qma.KERNEL_LARGE_M and moe.plan2.kernel == qma.KERNEL_LARGE_M
+    assert moe.plan13.kernel in qma.LARGE_M_KERNELS and moe.plan2.kernel in qma.LARGE_M_KERNELS
+    moe.plan13.kernel = moe.plan2.kernel = qma.KERNEL_LARGE_M
     moe.plan13.split_k = 2
     moe.plan2.split_k = 2
     moe.ws13 = workspace_for(moe.plan13)

@@ -179,6 +179,10 @@ def test_large_m_rule():
     assert _plan(48, 4096, 7168, 48 * 79, 1).kernel == qma.KERNEL_SMALL_M
     p = _plan(8, 256, 256, 64, 2, force=128)
     assert p.kernel == qma.KERNEL_LARGE_M and p.block_m == 128 and p.block_n == 256
+    # the producer/consumer form is never planned, split or not
+    assert p.split_k == 1                               # K = 256: no room to split
+    q = _plan(1, 4096, 7168, 200, 1, force=128)        # 32 tiles: split-K on
+    assert q.split_k > 1 and q.kernel == qma.KERNEL_LARGE_M
     # contiguous: every 128-row tile holds one expert, so large-M whatever M/E
     lay = qma.qma_layer_create(48, 4096, 7168, qma.PATH_GROUPED_CONTIGUOUS)
     try:
@@ -271,6 +275,12 @@ def test_host_checks_before_any_launch(L):
                 qma.qma_indexed_gemm(lay, big, fake, 64, 2, fake, fake, fake, fake, 1 << 12, 128,
                                      None, fake, fake, 1 << 30, stream=0)
             assert e12.value.status == qma.QMA_ERR_INVALID_ARG and "split_k" in e12.value.detail
+        pc = qma.qma_plan_indexed(lay, 64, 2, 128)
+        pc.kernel, pc.split_k = qma.KERNEL_LARGE_M_PC, 2      # no split-K in this form
+        with pytest.raises(qma.QmaError) as e13:
+            qma.qma_indexed_gemm(lay, pc, fake, 64, 2, fake, fake, fake, fake, 1 << 12, 128,
+                                 None, fake, fake, 1 << 30, stream=0)
+        assert e13.value.status == qma.QMA_ERR_INVALID_ARG
         # edited plans naming no kernel instance: 8 column tiles per wave,
         # waves_k 3, a streamed 64-column block
         for edit in ({"block_m": 16, "block_n": 128, "waves_k": 4, "split_k": 1},

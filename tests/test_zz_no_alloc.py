@@ -59,8 +59,8 @@ FAMILIES = {
                                            "n_stream": 1, "schedule": 1}),
                 (2, 9, 1, 512, 512, 16, {"block_n": 128, "waves_k": 1, "split_k": 1,
                                          "n_stream": 1, "schedule": 1})),
-    "large_m_split": ((2, 300, 1, 1024, 512, 128, {"split_k": 4}),
-                      (1, 90, 1, 512, 256, 128, {"split_k": 2})),
+    "large_m_split": ((2, 300, 1, 1024, 512, 128, {"split_k": 4, "kernel": 2}),
+                      (1, 90, 1, 512, 256, 128, {"split_k": 2, "kernel": 2})),
 }
 
 
