@@ -104,7 +104,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     // Between one and two workgroups per CU with long K (an EP32 gate_up
     // share: 384 tiles), two wave pairs splitting K keep more weight loads in
     // flight per workgroup than four waves side by side (measured 52 vs
-    // 60 us); split-K only adds a reduction there.
+    // 60 us). At three chunks in flight per wave this ran 50.5-50.8 us,
+    // against 52.0 us at four and 51.6-51.8 us for the shared-row kernel
+    // with split-K 2 (same box).
     const int64_t t128 = L.N % 128 == 0 ? (int64_t)tiles_m * (L.N / 128) : 0;
     if (tm == 1 && L.k_chunks >= 4 * qma::kStreamChunks && t128 >= qma::kNumCUs &&
         t128 < 2 * qma::kNumCUs) {
@@ -112,16 +114,11 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
       ntw = 4;
     }
   } else {
-    // 64-row tiles: the four waves split K in two when K is long (each wave
-    // still streams >= 12 chunks of 128) and split the columns otherwise.
-    wk = L.k_chunks >= 24 ? 2 : 1;
-    if (L.N % (16 * (4 / wk)) != 0) wk = 4;
-    const int wn0 = 4 / wk;
-    for (int cand : {4, 2, 1})
-      if (!ntw && qma::small_m_supported(tm, cand) && L.N % (16 * wn0 * cand) == 0) ntw = cand;
-    if (ntw == 4 && (int64_t)tiles_m * (L.N / (16 * wn0 * 4)) < qma::kNumCUs &&
-        L.N % (16 * wn0 * 2) == 0)
-      ntw = 2;
+    // 64-row tiles: the shared-row kernel at 128 columns (four waves side by
+    // side, two column tiles each), its rows staged once per workgroup; an
+    // underfilled grid is left to split-K as above.
+    wk = 1;
+    ntw = 2;
   }
   if (L.N % (16 * (4 / wk) * ntw) != 0) {
     // odd widths (N a multiple of 16 only): one tile per wave, waves on K
@@ -146,7 +143,7 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
   // chunks in flight per wave at three workgroups per CU
   int depth = tm <= 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw);
-  if (tm == 1 && wk == 2 && split == 1) depth = 4;  // the K-split pairs above
+  if (tm == 1 && wk == 2 && split == 1) depth = 3;  // the K-split pairs above
   p->k_depth = depth * qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
   // only one or two chunks would spend its life on start-up and one memory
@@ -266,7 +263,7 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
     const int wk = plan->waves_k;
     const int wn = (wk == 1 || wk == 2 || wk == 4) ? 4 / wk : 0;
     if (!wn || plan->block_n % (16 * wn) != 0 ||
-        !qma::small_m_supported(plan->block_m / 16, plan->block_n / (16 * wn)))
+        !qma::small_m_supported(plan->block_m / 16, plan->block_n / (16 * wn), wk))
       return fail(QMA_ERR_INVALID_ARG, "no small-M kernel for a %d x %d block with waves_k %d",
                   plan->block_m, plan->block_n, wk);
   }

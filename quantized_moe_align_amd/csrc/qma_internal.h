@@ -105,13 +105,26 @@ namespace qma {
 // Small-M kernel instances: TM = 16-token tiles per workgroup (1, 2 or 4),
 // NTW = 16-column weight tiles per wave (1, 2 or 4). A workgroup has 4 waves;
 // waves_k of them split K and 4 / waves_k split the columns, so
-// block_n = 16 * NTW * (4 / waves_k). The cross-wave reduction holds up to
-// 4 x NTW x TM KiB of LDS, so TM * NTW <= 8. The prefetch depth (128-wide K
-// chunks in flight per wave) is sized to a ~160 VGPR budget.
-constexpr bool small_m_supported(int tm, int ntw) {
-  return (tm == 1 || tm == 2 || tm == 4) && (ntw == 1 || ntw == 2 || ntw == 4) &&
-         tm * ntw <= 8;
+// block_n = 16 * NTW * (4 / waves_k).
+// * Shared-row kernel: the four waves side by side (waves_k 1) over 2 or 4
+//   column tiles each, the token rows staged once per workgroup in LDS;
+//   TM * NTW <= 8 accumulator tiles per wave.
+// * Per-wave-row kernel: every other shape (waves splitting K, or one
+//   column tile per wave). Each wave holds its token rows in registers for
+//   the whole prefetch depth, so only TM * NTW <= 4 fits the register file
+//   without spilling.
+constexpr bool small_m_shared_rows(int tm, int ntw, int wk) {
+  return wk == 1 && (tm == 1 || tm == 2 || tm == 4) && (ntw == 2 || ntw == 4) && tm * ntw <= 8;
 }
+constexpr bool small_m_wave_rows(int tm, int ntw, int wk) {
+  return (wk == 2 || wk == 4 || (wk == 1 && ntw == 1)) && (tm == 1 || tm == 2 || tm == 4) &&
+         (ntw == 1 || ntw == 2 || ntw == 4) && tm * ntw <= 4;
+}
+constexpr bool small_m_supported(int tm, int ntw, int wk) {
+  return small_m_shared_rows(tm, ntw, wk) || small_m_wave_rows(tm, ntw, wk);
+}
+// The prefetch depth (128-wide K chunks in flight per wave) of the
+// per-wave-row kernel, sized to a ~160 VGPR budget.
 constexpr int small_m_depth(int tm, int ntw) {
   const int per = ntw * 6 + tm * 16;
   const int fixed = ntw * tm * 4 + tm * 4 + 30;

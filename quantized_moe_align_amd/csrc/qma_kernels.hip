@@ -18,6 +18,7 @@ namespace qma {
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -366,6 +367,37 @@ __device__ __forceinline__ RowInfo row_info(const GemmParams& p, int tile, int e
   return ri;
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
+}
+
+// bytes 2H, 2H+1 of v (each 0..15) -> two exact floats
+template <bool H>
+__device__ __forceinline__ f32x2 byte_pair(uint32_t v) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.0f, H);
+}
+
+// One packed word (k0 k4 k1 k5 k2 k6 k3 k7) -> bf16((q - 8) s) for k0..k7
+// in order: two nibbles at a time become exact floats (a byte holding q in
+// 0..15, read as an OCP e4m3 code with power-of-two scale 512, is exactly q),
+// then q s - 8 s is one fp32 FMA, rounded once to bf16. About 19 VALU per
+// word, whatever the number of token rows that share it.
+__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
+  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes k0 k1 k2 k3
+  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes k4 k5 k6 k7
+  const f32x2 q01 = byte_pair<false>(lo), q23 = byte_pair<true>(lo);
+  const f32x2 q45 = byte_pair<false>(hi), q67 = byte_pair<true>(hi);
+  return u32x4{cvt_pk_bf16(__builtin_fmaf(q01.x, s, neg8s), __builtin_fmaf(q01.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q23.x, s, neg8s), __builtin_fmaf(q23.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q45.x, s, neg8s), __builtin_fmaf(q45.y, s, neg8s)),
+               cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
+}
+
+
 // One packed word -> the eight exact bf16 values 128 + q, in k order: the
 // bf16 pattern 0x43qq is 128 + q, so each output word is two value bytes
 // interleaved with the constant 0x43 (v_perm_b32 byte selects).
@@ -558,6 +590,20 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   auto compute = [&](const Stage& s) {
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
+      if constexpr (NTW == 1) {
+        // one column tile: each row tile's zero-point sum is used once, so
+        // it is formed just before its product (same operations and order)
+        const u32x4 wb = unpack_128q(s.w[0][g]);
+        const uint32_t sw = s.s[0][g >> 1];
+        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const f32x4 pr = mfma16(s.x[tm][g], wb, mfma16(s.x[tm][g], neg136, zero4));
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[0][tm][r] = __builtin_fmaf(scv, pr[r], acc[0][tm][r]);
+        }
+        continue;
+      }
       f32x4 xs[TM];
 #pragma unroll
       for (int tm = 0; tm < TM; ++tm) xs[tm] = mfma16(s.x[tm][g], neg136, zero4);
@@ -810,24 +856,28 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 }
 
 // Small-M variant with the token rows shared by the workgroup: TM 16-token
-// tiles, one K partition, the four waves side by side over 16 * NTW columns
-// each, n_stream column blocks streamed as in the kernel above. A chunk's
-// token rows (TM * 16 rows x 256 bytes) go through a ring of D LDS buffers,
-// each wave copying a quarter of them with direct-to-LDS loads (slot j of
-// row r holds segment j ^ (r % 16)); weights go through D register stages
-// per wave. One bare barrier per chunk: at step j every wave has its own
-// loads of chunk j (wait count) and, past the barrier, every wave is done
-// with chunk j-1, whose buffer then takes chunk j+D-1. Sharing the rows
-// keeps the LDS (D * TM * 4 KiB) and register budget small enough for three
+// tiles and one column block of 64 * NTW columns, the four waves side by
+// side over 16 * NTW columns each. Without split-K a workgroup runs the
+// whole K; with it, workgroup sp of a (tile, column block) runs the sp-th K
+// range and writes fp32 partials for the ordered reduction. A chunk's token
+// rows (TM * 16 rows x 256 bytes) go through a ring of D LDS buffers, each
+// wave copying a quarter of them with direct-to-LDS loads (slot j of row r
+// holds segment j ^ (r % 16)); weights go through D register stages per
+// wave. One bare barrier per chunk: at step j every wave has its own loads
+// of chunk j (wait count) and, past the barrier, every wave is done with
+// chunk j-1, whose buffer then takes chunk j+D-1. Sharing the rows keeps the
+// LDS (D * TM * 4 KiB) and register budget small enough for three
 // workgroups per CU, which decode grids need to keep HBM busy, and loads
 // each row once per workgroup instead of once per wave.
 template <int TM, int D>
-constexpr int xs_lds_bytes() { return D * TM * 16 * 256; }
+constexpr int xs_lds_bytes() { return D * TM * 16 * 256 + TM * 16 * 8; }
 
-// One (token tile, column group) of the shared-row kernel; s_x holds
-// xs_lds_bytes<TM, D>() bytes of LDS.
+// One (token tile, column block, K split) of the shared-row kernel; s_x
+// holds xs_lds_bytes<TM, D>() bytes of LDS: the D token buffers, then the
+// tile's output rows and topk weights (TM * 16 of each).
 template <int TM, int NTW, int D>
-__device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, uint8_t* s_x) {
+__device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, int sp,
+                                        uint8_t* s_x) {
   constexpr int XROW = 256;
   constexpr int XBUF = TM * 16 * XROW;       // one chunk of the tile's token rows
   constexpr int NX = TM;                     // direct-to-LDS loads per wave and chunk
@@ -840,14 +890,21 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
   const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int col = lane & 15, kb = lane >> 4;
   const int KC = p.KC;
-  const int nb0 = grp * p.nstream;
-  const int total = min(p.nstream, p.nbtot - nb0) * KC;
+  // this workgroup's K range (all of K without split-K; the host keeps
+  // split_k <= K / 128, so every range holds a chunk)
+  const int cs0 = (int)(((int64_t)sp * KC) / p.split);
+  const int total = (int)(((int64_t)(sp + 1) * KC) / p.split) - cs0;
+  if (total <= 0) return;
 
+  // weights and scales of this column block: wave w owns its 16-column
+  // tiles (nb * 4 + w) * NTW + nt
+  const int nt0 = nb * 4 * NTW;
   const uint32_t tile_bytes = (uint32_t)KC * kWBlockBytes;
   const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(p.wpk + (size_t)e * p.NT * tile_bytes, (uint32_t)p.NT * tile_bytes);
+      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, 4u * NTW * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.spk + (size_t)e * p.NT * KC * kSBlockBytes, (uint32_t)p.NT * KC * kSBlockBytes);
+      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * KC * kSBlockBytes,
+                4u * NTW * KC * kSBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
   const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
   const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
@@ -860,46 +917,41 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
     const uint32_t seg = (uint32_t)(col ^ (row & 15));
     voff_x[i] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
-  int32_t out_row[TM][4];
-  float tw[TM][4];
-#pragma unroll
-  for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const RowInfo ri = row_info(p, tile, e, tm * 16 + kb * 4 + r);
-      out_row[tm][r] = ri.valid ? ri.out_row : -1;
-      tw[tm][r] = (ri.valid && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
-    }
+  // The tile's output rows and topk weights: wave 0 looks them up here,
+  // so that the loads overlap the pipeline's start, and parks them in LDS
+  // after the prologue; the K loop holds no registers for them.
+  int32_t* s_orow = (int32_t*)(s_x + D * XBUF);
+  float* s_tw = (float*)(s_orow + TM * 16);
+  const bool scale_rows = p.split == 1 && p.mode == 0 && p.topk_w;
+  int32_t my_orow = -1;
+  float my_tw = 1.0f;
+  if (w == 0 && lane < TM * 16) {
+    const RowInfo ri = row_info(p, tile, e, lane);
+    my_orow = ri.valid ? ri.out_row : -1;
+    my_tw = (ri.valid && scale_rows) ? p.topk_w[ri.out_row] : 1.0f;
+  }
 
-  // stream position f -> (column block, chunk); past the end the last
-  // chunk is fetched again, so every step issues the same loads
-  auto pos = [&](int f, int& nb, int& c) {
-    f = min(f, total - 1);
-    const int q = f / KC;
-    nb = nb0 + q;
-    c = f - q * KC;
-  };
+  // step f -> K chunk; past the end the last chunk is fetched again, so
+  // every step issues the same loads
+  auto chunk = [&](int f) { return cs0 + min(f, total - 1); };
   struct WStage {
     u32x4 w[NTW];
     u32x2 s[NTW];
   };
   auto load_w = [&](WStage& st, int f) {
-    int nb, c;
-    pos(f, nb, c);
-    const int t0 = nb * 4 * NTW;
+    const int c = chunk(f);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, voff_w, (t0 + nt) * tile_bytes + c * kWBlockBytes, kNonTemporal);
+      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w,
+                                                       nt * tile_bytes + c * kWBlockBytes,
+                                                       kNonTemporal);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
-                                                      ((t0 + nt) * KC + c) * kSBlockBytes, 0);
+      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, (nt * KC + c) * kSBlockBytes, 0);
   };
   auto load_x = [&](auto buf_id, int f) {
     constexpr int b = decltype(buf_id)::value;
-    int nb, c;
-    pos(f, nb, c);
+    const int c = chunk(f);
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int vo = (int)voff_x[i];
@@ -920,20 +972,29 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
   // operand read: row tm*16 + l%16, segment 4g + l/16 at slot segment ^ (l%16)
   const uint32_t xrd = lds_addr(s_x) + col * XROW;
 
-  int c_nb = nb0, c_c = 0;
+  // Four token tiles share each weight word: dequantising it once to
+  // bf16((q - 8) s) (about 19 VALU) then costs less than the exact form's
+  // per-tile scale FMAs (4 per tile) and zero-point MFMAs, and the MFMAs
+  // accumulate straight into acc. Fewer tiles keep the exact form.
+  constexpr bool kScaledW = TM >= 4;
   auto compute = [&](auto buf_id, const WStage& st) {
     constexpr int b = decltype(buf_id)::value;
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const uint32_t a = xrd + b * XBUF + (((4 * g + kb) ^ col) << 4);
       u32x4 xg[TM];
-      xg[0] = lds_read16<0>(a);
-      if constexpr (TM > 1) xg[1] = lds_read16<16 * XROW>(a);
-      if constexpr (TM > 1) {
-        wait_lgkm<1>(xg[0]);
-        wait_lgkm<0>(xg[1]);
-      } else {
-        wait_lgkm<0>(xg[0]);
+      static_for<TM>([&](auto tm) { xg[tm] = lds_read16<tm * 16 * XROW>(a); });
+      static_for<TM>([&](auto tm) { wait_lgkm<TM - 1 - tm>(xg[tm]); });
+      if constexpr (kScaledW) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const uint32_t sw = st.s[nt][g >> 1];
+          const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+          const u32x4 wb = dequant8(st.w[nt][g], scv, -8.0f * scv);
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = mfma16(xg[tm], wb, acc[nt][tm]);
+        }
+        continue;
       }
       f32x4 xsum[TM];
 #pragma unroll
@@ -951,23 +1012,6 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
         }
       }
     }
-    if (++c_c == KC) {
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            if (out_row[tm][r] >= 0)
-              p.c[(size_t)out_row[tm][r] * p.N + n] =
-                  (uint16_t)(pack_bf16x2(acc[nt][tm][r] * tw[tm][r], 0.f) & 0xFFFFu);
-            acc[nt][tm][r] = 0.f;
-          }
-      }
-      c_c = 0;
-      ++c_nb;
-    }
   };
 
   // Pipeline. Issue order: prologue W(0) X(0) W(1) X(1) .. X(D-2) W(D-1);
@@ -982,6 +1026,10 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
     __builtin_amdgcn_sched_barrier(0);
   });
   load_w(ws[D - 1], D - 1);
+  if (w == 0 && lane < TM * 16) {
+    s_orow[lane] = my_orow;
+    s_tw[lane] = my_tw;
+  }
   auto step = [&](int j, auto cur) {
     constexpr int b = decltype(cur)::value;
     wait_vmcnt<kAfter>();
@@ -1003,17 +1051,40 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int grp, 
     if (done) break;
   }
   wait_vmcnt<0>();
+  // every wave's view of the row table (a one-chunk range has had no
+  // barrier since wave 0 wrote it)
+  __syncthreads();
+
+  // Output: lane holds rows tm*16 + 4*kb + r of column col of each tile.
+#pragma unroll
+  for (int tm = 0; tm < TM; ++tm) {
+    const i32x4 orow = *(const i32x4*)(s_orow + tm * 16 + kb * 4);
+    const f32x4 twv = *(const f32x4*)(s_tw + tm * 16 + kb * 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      if (orow[r] < 0) continue;
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const int n = (nt0 + w * NTW + nt) * 16 + col;
+        if (p.split > 1)
+          p.ws[((size_t)sp * p.rows_cap + orow[r]) * p.N + n] = acc[nt][tm][r];
+        else
+          p.c[(size_t)orow[r] * p.N + n] =
+              (uint16_t)(pack_bf16x2(acc[nt][tm][r] * twv[r], 0.f) & 0xFFFFu);
+      }
+    }
+  }
 }
 
 // Semi-static schedule: the grid covers every (tile, column group) the
 // host can bound; a workgroup derives its item from its index and the
 // routing buffers, and items past the routed ones exit at once.
 template <int TM, int NTW, int D>
-__global__ __launch_bounds__(256, 3) void gemm_small_m_xs_kernel(const GemmParams p) {
+__global__ __launch_bounds__(256, 4) void gemm_small_m_xs_kernel(const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[xs_lds_bytes<TM, D>()];
   int tile, grp, sp;
   if (!decode_bid(p, tile, grp, sp)) return;
-  xs_tile<TM, NTW, D>(p, tile, grp, s_x);
+  xs_tile<TM, NTW, D>(p, tile, grp, sp, s_x);
 }
 
 // Dynamic schedule: a persistent grid whose workgroups take (tile, column
@@ -1030,7 +1101,7 @@ __global__ __launch_bounds__(256, 3) void gemm_small_m_xs_dyn_kernel(const GemmP
     const int it = __builtin_amdgcn_readfirstlane(s_item);
     if (it >= items) break;
     const int tile = it / p.nblocks;
-    xs_tile<TM, NTW, D>(p, tile, it - tile * p.nblocks, s_x);
+    xs_tile<TM, NTW, D>(p, tile, it - tile * p.nblocks, 0, s_x);
     // every wave is done with s_item and the LDS ring before the next item
     __syncthreads();
   }
@@ -1135,39 +1206,12 @@ constexpr int kLmMT = kLmBM / 32;   // 32-row tiles per wave
 constexpr int kLmNT = 2;            // 32-column tiles per wave
 constexpr int kLmBLoads = 3 * kLmNT;  // weight + scale loads per chunk and wave
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
-
-__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2v));
-}
-
-// bytes 2H, 2H+1 of v (each 0..15) -> two exact floats
-template <bool H>
-__device__ __forceinline__ f32x2 byte_pair(uint32_t v) {
-  return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(v, 512.0f, H);
-}
-
-// One packed word (k0 k4 k1 k5 k2 k6 k3 k7) -> bf16((q - 8) s) for k0..k7
-// in order.
-__device__ __forceinline__ u32x4 dequant8(uint32_t w, float s, float neg8s) {
-  const uint32_t lo = w & 0x0F0F0F0Fu;          // bytes k0 k1 k2 k3
-  const uint32_t hi = (w >> 4) & 0x0F0F0F0Fu;   // bytes k4 k5 k6 k7
-  const f32x2 q01 = byte_pair<false>(lo), q23 = byte_pair<true>(lo);
-  const f32x2 q45 = byte_pair<false>(hi), q67 = byte_pair<true>(hi);
-  return u32x4{cvt_pk_bf16(__builtin_fmaf(q01.x, s, neg8s), __builtin_fmaf(q01.y, s, neg8s)),
-               cvt_pk_bf16(__builtin_fmaf(q23.x, s, neg8s), __builtin_fmaf(q23.y, s, neg8s)),
-               cvt_pk_bf16(__builtin_fmaf(q45.x, s, neg8s), __builtin_fmaf(q45.y, s, neg8s)),
-               cvt_pk_bf16(__builtin_fmaf(q67.x, s, neg8s), __builtin_fmaf(q67.y, s, neg8s))};
-}
-
 
 // Rows of a tile that hold no token are never computed: the tile's valid
 // rows are counted first, and only the 32-row groups that hold any of them
@@ -1936,9 +1980,9 @@ template <int TM, int NTW, int WK>
 static int launch_small_m_depth(const GemmParams& gp, unsigned grid, hipStream_t st, int depth) {
   constexpr int D0 = small_m_depth(TM, NTW);
   if constexpr (TM == 1 && NTW == 4) {
+    // depth 4 would need more than 256 VGPRs and spill
     if (depth == 2) return launch_small_m_inst<TM, NTW, WK, 2>(gp, grid, st);
     if (depth == 3) return launch_small_m_inst<TM, NTW, WK, 3>(gp, grid, st);
-    if (depth == 4) return launch_small_m_inst<TM, NTW, WK, 4>(gp, grid, st);
   }
   return launch_small_m_inst<TM, NTW, WK, D0>(gp, grid, st);
 }
@@ -1946,7 +1990,8 @@ static int launch_small_m_depth(const GemmParams& gp, unsigned grid, hipStream_t
 template <int TM, int NTW>
 static int launch_small_m_wk(const GemmParams& gp, unsigned grid, hipStream_t st, int wk,
                              int depth) {
-  if (wk == 1) return launch_small_m_depth<TM, NTW, 1>(gp, grid, st, depth);
+  if constexpr (small_m_wave_rows(TM, NTW, 1))
+    if (wk == 1) return launch_small_m_depth<TM, NTW, 1>(gp, grid, st, depth);
   if (wk == 2) return launch_small_m_depth<TM, NTW, 2>(gp, grid, st, depth);
   if (wk == 4) return launch_small_m_depth<TM, NTW, 4>(gp, grid, st, depth);
   return (int)hipErrorInvalidConfiguration;
@@ -2014,10 +2059,10 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   const int wk = pl.waves_k;
   const int ntw = pl.block_n / (16 * (4 / std::max(wk, 1)));
   const int depth = pl.k_depth / kChunkK;
-  const bool xs = (tm == 1 || tm == 2) && wk == 1 && gp.split == 1 && pl.n_stream == 1 &&
-                  (ntw == 2 || ntw == 4);
+  const bool xs = small_m_shared_rows(tm, ntw, wk) && ntw * 64 == pl.block_n && pl.n_stream == 1;
   if (pl.schedule == QMA_SCHEDULE_DYNAMIC) {
-    if (!xs || g.ws == nullptr) return (int)hipErrorInvalidConfiguration;
+    if (!xs || tm > 2 || gp.split != 1 || g.ws == nullptr)
+      return (int)hipErrorInvalidConfiguration;
     gp.nstream = 1;
     gp.nbtot = gp.nblocks;
     gp.work = (int32_t*)g.ws;
@@ -2033,45 +2078,46 @@ int launch_gemm(const GemmArgs& g, void* stream) {
       hipLaunchKernelGGL((gemm_small_m_xs_dyn_kernel<2, 2, 2>), dg, dim3(256), 0, st, gp);
     return (int)hipGetLastError();
   }
+  int err = (int)hipErrorInvalidConfiguration;
   if (pl.n_stream > 1 || xs) {
-    // one K partition: 16-row tiles streaming column blocks, or 16/32-row
-    // tiles with the token rows shared through LDS
-    if (wk != 1 || gp.split != 1 || (ntw != 2 && ntw != 4) || ntw * 64 != pl.block_n ||
-        (pl.n_stream > 1 && tm != 1))
+    // one K partition per workgroup: 16-row tiles streaming column blocks,
+    // or 16/32/64-row tiles with the token rows shared through LDS (these
+    // also take split-K)
+    if (wk != 1 || (ntw != 2 && ntw != 4) || ntw * 64 != pl.block_n ||
+        (pl.n_stream > 1 && (tm != 1 || gp.split != 1)))
       return (int)hipErrorInvalidConfiguration;
     gp.nstream = pl.n_stream;
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
-    const dim3 sg((unsigned)(tiles_pad * gp.nblocks));
+    const dim3 sg((unsigned)(tiles_pad * gp.nblocks * gp.split));
     if (xs && tm == 1 && ntw == 4)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 4, 2>), sg, dim3(256), 0, st, gp);
     else if (xs && tm == 1)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 2, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs && ntw == 4)
+    else if (xs && tm == 2 && ntw == 4)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 4, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs)
+    else if (xs && tm == 2)
       hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);
+    else if (xs)
+      hipLaunchKernelGGL((gemm_small_m_xs_kernel<4, 2, 2>), sg, dim3(256), 0, st, gp);
     else if (ntw == 4)
       hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), sg, dim3(256), 0, st, gp);
     else
       hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), sg, dim3(256), 0, st, gp);
-    return (int)hipGetLastError();
-  }
-  if (!small_m_supported(tm, ntw) || (wk != 1 && wk != 2 && wk != 4) ||
-      ntw * 16 * (4 / wk) != pl.block_n)
-    return (int)hipErrorInvalidConfiguration;
-  int err = (int)hipErrorInvalidConfiguration;
+    err = (int)hipGetLastError();
+  } else {
+    if (!small_m_wave_rows(tm, ntw, wk) || ntw * 16 * (4 / wk) != pl.block_n)
+      return (int)hipErrorInvalidConfiguration;
 #define QMA_SMALL_M_CASE(TM_, NTW_) \
   if (tm == TM_ && ntw == NTW_) err = launch_small_m_wk<TM_, NTW_>(gp, (unsigned)grid, st, wk, depth);
-  QMA_SMALL_M_CASE(1, 1)
-  QMA_SMALL_M_CASE(1, 2)
-  QMA_SMALL_M_CASE(1, 4)
-  QMA_SMALL_M_CASE(2, 1)
-  QMA_SMALL_M_CASE(2, 2)
-  QMA_SMALL_M_CASE(2, 4)
-  QMA_SMALL_M_CASE(4, 1)
-  QMA_SMALL_M_CASE(4, 2)
+    QMA_SMALL_M_CASE(1, 1)
+    QMA_SMALL_M_CASE(1, 2)
+    QMA_SMALL_M_CASE(1, 4)
+    QMA_SMALL_M_CASE(2, 1)
+    QMA_SMALL_M_CASE(2, 2)
+    QMA_SMALL_M_CASE(4, 1)
 #undef QMA_SMALL_M_CASE
+  }
   if (err != 0) return err;
   if (gp.split > 1) {
     const int64_t total = (int64_t)gp.num_tiles * gp.BM * (gp.N / 4);

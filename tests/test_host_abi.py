@@ -114,8 +114,8 @@ def test_plan_tp8_and_tiny():
     assert d.waves_k == 1 and d.block_n == 128 and d.split_k == 1
     m = _plan(48, 4096, 7168, 48 * 32, 1)              # 32-row tiles: 256 columns
     assert m.block_m == 32 and m.waves_k == 1 and m.block_n == 256
-    big = _plan(48, 4096, 7168, 48 * 64, 1)            # 64-row tiles: K split in two
-    assert big.block_m == 64 and big.waves_k == 2
+    big = _plan(48, 4096, 7168, 48 * 64, 1)            # 64-row tiles: shared rows, 128 wide
+    assert big.block_m == 64 and big.waves_k == 1 and big.block_n == 128 and big.split_k == 1
 
 
 def test_block_m_follows_tok_e():
@@ -133,7 +133,7 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> no split; between one
     # and two workgroups per CU the waves split K in pairs (128 columns)
     q = _plan(12, 4096, 7168, 144, 1)
-    assert q.split_k == 1 and q.block_n == 128 and q.waves_k == 2 and q.k_depth == 512
+    assert q.split_k == 1 and q.block_n == 128 and q.waves_k == 2 and q.k_depth == 384
     # EP32 down (672 tiles) and EP16 gate_up (768 tiles): four waves side by side
     d = _plan(12, 7168, 2048, 144, 1)
     assert d.split_k == 1 and d.block_n == 128 and d.waves_k == 1
@@ -282,10 +282,13 @@ def test_host_checks_before_any_launch(L):
                                  None, fake, fake, 1 << 30, stream=0)
         assert e13.value.status == qma.QMA_ERR_INVALID_ARG
         # edited plans naming no kernel instance: 8 column tiles per wave,
-        # waves_k 3, a streamed 64-column block
+        # waves_k 3, 16 accumulator tiles per wave, 8 with rows held per wave,
+        # a streamed 64-column block
         for edit in ({"block_m": 16, "block_n": 128, "waves_k": 4, "split_k": 1},
                      {"block_m": 16, "block_n": 128, "waves_k": 3, "split_k": 1},
                      {"block_m": 64, "block_n": 256, "waves_k": 1, "split_k": 1},
+                     {"block_m": 64, "block_n": 128, "waves_k": 2, "split_k": 1},
+                     {"block_m": 32, "block_n": 64, "waves_k": 4, "split_k": 1},
                      {"block_m": 16, "block_n": 64, "waves_k": 1, "split_k": 1, "n_stream": 2}):
             q = qma.Plan.from_buffer_copy(qma.qma_plan_indexed(lay, 64, 2))
             for k, v in edit.items():
@@ -335,7 +338,11 @@ def test_planner_invariants_over_shapes():
         else:
             assert p.kernel == qma.KERNEL_SMALL_M and p.block_m in (16, 32, 64), shape
             tm, ntw = p.block_m // 16, p.block_n // (16 * (4 // p.waves_k))
-            assert tm * ntw <= 8 and ntw in (1, 2, 4), shape
+            assert ntw in (1, 2, 4), shape
+            # a compiled instance: shared rows (waves_k 1, 2 or 4 column tiles
+            # per wave, at most 8 accumulator tiles) or rows per wave (at most 4)
+            shared = p.waves_k == 1 and ntw in (2, 4) and tm * ntw <= 8
+            assert shared or tm * ntw <= 4, shape
             if p.n_stream > 1:                               # streaming: short K only
                 assert K // 128 < 8 and p.block_m == 16 and p.split_k == 1, shape
         if p.split_k > 1:
