@@ -115,11 +115,14 @@ typedef enum qma_kernel {
  * block_m, block_n, split_k, k_depth, waves_k, n_stream and schedule; the
  * GEMM calls validate the plan against the layer and reject, with
  * QMA_ERR_INVALID_ARG and before any launch, a plan made for another layer
- * or one that names no compiled kernel instance (small-M: block_m in
- * {16, 32, 64}, waves_k in {1, 2, 4}, at most 8 16x16 tiles per wave;
- * large-M: a 128 x 256 block, and split_k = 1 for the producer/consumer
- * form), or whose split_k is outside [1, 8] or above
- * K/128 (every K partition owns at least one 128-wide chunk). k_depth
+ * or one that names no compiled kernel instance, or whose split_k is
+ * outside [1, 8] or above K/128 (every K partition owns at least one
+ * 128-wide chunk). Compiled instances: small-M with block_m in {16, 32, 64}
+ * and waves_k in {1, 2, 4}, where a wave owns block_n / (16 * 4 / waves_k)
+ * 16-column tiles (1, 2 or 4) and block_m / 16 row tiles; waves_k = 1 with
+ * 2 or 4 column tiles takes up to 8 (row x column) tiles per wave, every
+ * other small-M shape up to 4; large-M: a 128 x 256 block, and split_k = 1
+ * for the producer/consumer form. k_depth
  * outside an instance's supported depths falls back to that instance's
  * default. */
 typedef struct qma_plan {

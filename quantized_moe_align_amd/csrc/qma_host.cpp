@@ -87,8 +87,11 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     ntw = (tm == 2 || L.k_chunks < qma::kStreamChunks) ? 4 : 2;
     while (ntw > 1 && L.N % (64 * ntw) != 0) ntw /= 2;
     // Wave-aware width: the narrower width when the wide one leaves CUs
-    // without a workgroup; an underfilled grid is then left to split-K.
-    if (ntw > 1 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
+    // without a workgroup, down to 128 columns; an underfilled grid is then
+    // left to split-K. (64 columns would leave the shared-row kernel: on an
+    // EP128 share, 3 experts, that ran gate_up in 60.5 us at split 2 against
+    // 30.6 us at 128 columns and split 4, and down in 34.5 against 20.3 us.)
+    if (ntw > 2 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
         L.N % (64 * (ntw / 2)) == 0)
       ntw /= 2;
     // 16-row tiles with long K and wide N (>= 8 blocks of 256) take 256
@@ -131,12 +134,16 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   const int32_t tiles =
       (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / p->block_n), 1 << 30);
   p->est_tiles = tiles;
-  // Split-K gate: only when the grid underfills the CUs, and never below
-  // two 128-wide K chunks per wave.
+  // Split-K gate: only when the grid underfills the CUs. It then aims at
+  // 1.5 workgroups per CU, never below kSplitChunks 128-wide K chunks per
+  // split. (EP128 gate_up, 96 tiles, K = 56 chunks: split 3/4/6/8 ran
+  // 31.4/30.6/32.1/34.8 us; down, 168 tiles, K = 16 chunks: unsplit 20.3 us,
+  // split 2-3 21.2-23.6 us.)
   int32_t split = 1;
   if (tiles < qma::kNumCUs) {
-    const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / (2 * wk)));
-    split = std::min<int32_t>({ceil_div(qma::kNumCUs, std::max(tiles, 1)), max_split, 8});
+    const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / qma::kSplitChunks));
+    split = std::min<int32_t>(
+        {ceil_div(3 * qma::kNumCUs / 2, std::max(tiles, 1)), max_split, 8});
     split = std::max<int32_t>(split, 1);
   }
   p->split_k = split;

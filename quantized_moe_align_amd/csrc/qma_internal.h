@@ -31,6 +31,10 @@ constexpr int kStreamChunks = 8;
 // chunks). On the TP8 down share (K = 256, two chunks per block) 14 chunks
 // (7 blocks) ran 3-4 % faster than 8 and 28.
 constexpr int kStreamTargetChunks = 14;
+// fewest 128-wide K chunks a small-M split-K partition is planned with: a
+// shorter run pays the pipeline's start and the reduction for too little
+// streaming
+constexpr int kSplitChunks = 14;
 // bytes at the end of the workspace holding a dynamic schedule's counter
 constexpr int kWorkCounterBytes = 256;
 // size of the library's static device scratch (qma_indexed_gemm_scratch):

@@ -124,12 +124,19 @@ def test_block_m_follows_tok_e():
 
 
 def test_split_k_gate_turns_on_only_when_underfilled():
-    # 1 expert: 32 tiles at 128 columns, 64 at 64 < 256 CUs -> split
+    # 1 expert: 32 tiles at 128 columns < 256 CUs -> split toward 1.5
+    # workgroups per CU, capped at 56 / 14 = 4 K runs of 14 chunks
     p = _plan(1, 4096, 7168, 12, 1)
-    assert p.block_n == 64 and p.est_tiles == 64 and p.split_k == 4
+    assert p.block_n == 128 and p.est_tiles == 32 and p.split_k == 4 and p.waves_k == 1
     assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
-    # 4 experts: the 64-column width gives exactly 256 tiles -> no split
-    assert _plan(4, 4096, 7168, 48, 1).split_k == 1
+    # EP128 share (3 experts): gate_up 96 tiles -> split 4; down (K = 16
+    # chunks) has no room for two runs of 14 -> unsplit, still 128 wide
+    g = _plan(3, 4096, 7168, 35, 1)
+    assert g.block_n == 128 and g.est_tiles == 96 and g.split_k == 4
+    d = _plan(3, 7168, 2048, 35, 1)
+    assert d.block_n == 128 and d.est_tiles == 168 and d.split_k == 1
+    # 8 experts: 256 tiles at 128 columns -> no split
+    assert _plan(8, 4096, 7168, 96, 1).split_k == 1
     # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> no split; between one
     # and two workgroups per CU the waves split K in pairs (128 columns)
     q = _plan(12, 4096, 7168, 144, 1)
@@ -347,9 +354,9 @@ def test_planner_invariants_over_shapes():
                 assert K // 128 < 8 and p.block_m == 16 and p.split_k == 1, shape
         if p.split_k > 1:
             # split-K only when the grid underfills the CUs, and never below
-            # two 128-wide K chunks per wave (four per split for large-M)
+            # 14 128-wide K chunks per split (four for large-M)
             assert p.est_tiles < 256, shape
-            per_split = 4 if p.kernel == qma.KERNEL_LARGE_M else 2 * p.waves_k
+            per_split = 4 if p.kernel == qma.KERNEL_LARGE_M else 14
             assert K // 128 >= per_split * p.split_k, shape
             assert qma.qma_workspace_bytes(p) > 0, shape
         else:

@@ -54,7 +54,7 @@ def _call(rng, E, T, topk, K, N, force_bm=0, override=None):
 FAMILIES = {
     "small_m_split": ((3, 40, 2, 2048, 1024, 16, {"split_k": 4, "block_n": 64, "waves_k": 4}),
                       (1, 12, 1, 1024, 512, 16, {"split_k": 2, "block_n": 64, "waves_k": 4})),
-    "planner_split": ((1, 12, 1, 2048, 4096, 0, None), (1, 5, 1, 1024, 2048, 0, None)),
+    "planner_split": ((1, 12, 1, 4096, 4096, 0, None), (1, 5, 1, 4096, 2048, 0, None)),
     "dynamic": ((5, 60, 2, 1024, 768, 16, {"block_n": 256, "waves_k": 1, "split_k": 1,
                                            "n_stream": 1, "schedule": 1}),
                 (2, 9, 1, 512, 512, 16, {"block_n": 128, "waves_k": 1, "split_k": 1,
