@@ -588,6 +588,37 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   auto compute = [&](const Stage& s) {
+    if constexpr (TM == 1 && NTW == 4) {
+      // zero-point MFMAs first, then products one (group, column tile)
+      // pair ahead of their scale FMAs (same per-accumulator order as the
+      // loop below), so no MFMA result is read right after its issue
+      f32x4 xs[4];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) xs[g] = mfma16(s.x[0][g], neg136, zero4);
+      f32x4 pr[2];
+      float scv[2];
+      auto product = [&](int i) {
+        const int g = i / NTW, nt = i % NTW;
+        const u32x4 wb = unpack_128q(s.w[nt][g]);
+        const uint32_t sw = s.s[nt][g >> 1];
+        scv[i & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        pr[i & 1] = mfma16(s.x[0][g], wb, xs[g]);
+      };
+      auto scale = [&](int i) {
+        const int nt = i % NTW;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[nt][0][r] = __builtin_fmaf(scv[i & 1], pr[i & 1][r], acc[nt][0][r]);
+      };
+      product(0);
+#pragma unroll
+      for (int i = 1; i < 4 * NTW; ++i) {
+        product(i);
+        scale(i - 1);
+      }
+      scale(4 * NTW - 1);
+      return;
+    }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       if constexpr (NTW == 1) {
@@ -790,17 +821,50 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   // compute cursor: column block and chunk of the next stage to consume
   int c_nb = nb0, c_c = 0;
   auto step = [&](const Stage& s) {
+    if constexpr (NTW == 4) {
+      // The four zero-point MFMAs go first and products run one (group,
+      // column tile) pair ahead of their scale FMAs, so no MFMA result is
+      // read right after its issue; each accumulator takes the same
+      // operations in the same order as the plain loop below. (With two
+      // column tiles the extra registers would cost a workgroup per CU.)
+      f32x4 xs[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 xs = mfma16(s.x[g], neg136, zero4);
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
+      for (int g = 0; g < 4; ++g) xs[g] = mfma16(s.x[g], neg136, zero4);
+      f32x4 pr[2];
+      float scv[2];
+      auto product = [&](int i) {
+        const int g = i / NTW, nt = i % NTW;
         const u32x4 wb = unpack_128q(s.w[nt][g]);
         const uint32_t sw = s.s[nt][g >> 1];
-        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        const f32x4 pr = mfma16(s.x[g], wb, xs);
+        scv[i & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        pr[i & 1] = mfma16(s.x[g], wb, xs[g]);
+      };
+      auto scale = [&](int i) {
+        const int nt = i % NTW;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
+        for (int r = 0; r < 4; ++r)
+          acc[nt][r] = __builtin_fmaf(scv[i & 1], pr[i & 1][r], acc[nt][r]);
+      };
+      product(0);
+#pragma unroll
+      for (int i = 1; i < 4 * NTW; ++i) {
+        product(i);
+        scale(i - 1);
+      }
+      scale(4 * NTW - 1);
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4 xs = mfma16(s.x[g], neg136, zero4);
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const u32x4 wb = unpack_128q(s.w[nt][g]);
+          const uint32_t sw = s.s[nt][g >> 1];
+          const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+          const f32x4 pr = mfma16(s.x[g], wb, xs);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
+        }
       }
     }
     if (++c_c == KC) {
