@@ -4,8 +4,9 @@ The kernel file is compiled for gfx950 with the library's own device flags
 and the compiler's per-kernel resource remarks. Every kernel the planner or
 an edited plan can launch must run without scratch: a spilled VGPR turns
 into a private-memory round trip inside the K loop. The shared-row small-M
-instances must also fit four workgroups per compute unit (at most 128 VGPRs
-and a quarter of the LDS).
+instances must also fit the workgroups per compute unit they are built for
+(four: at most 128 VGPRs and a quarter of the LDS; three for the 32-row,
+4-tile instance).
 """
 import os
 import re
@@ -63,9 +64,11 @@ def test_no_kernel_uses_scratch(resources):
     assert not bad, bad
 
 
-def test_shared_row_instances_fit_four_workgroups(resources):
+def test_shared_row_instances_fit_their_occupancy(resources):
+    # four workgroups per CU, three for the 32-row 4-tile instance
     xs = {n: r for n, r in resources.items() if "gemm_small_m_xs_kernel" in n}
     assert len(xs) == 5, sorted(xs)            # (1,2) (1,4) (2,2) (2,4) (4,2)
     for n, r in xs.items():
-        assert r["VGPRs"] <= 128, (n, r["VGPRs"])
-        assert r["LDS Size"] <= 160 * 1024 // 4, (n, r["LDS Size"])
+        per_cu = 3 if "ILi2ELi4E" in n else 4
+        assert r["VGPRs"] <= 512 // per_cu // 8 * 8, (n, r["VGPRs"])
+        assert r["LDS Size"] <= 160 * 1024 // per_cu, (n, r["LDS Size"])
