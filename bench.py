@@ -52,8 +52,10 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 HBM_BOUND = {"ep8_decode", "tp8", "masked", "ep16_decode", "ep32_decode", "tiny", "ep8_mid",
              "ep128_decode"}
-# the pages' six measured scenarios map onto these workloads
-DEFAULT_CONFIGS = ("tiny", "ep8_decode", "tp8", "ep8_prefill", "contiguous", "masked")
+# the pages' six measured scenarios map onto the first six workloads; the last two
+# cover the 33..79 rows-per-expert regime and a share where split-K turns on
+DEFAULT_CONFIGS = ("tiny", "ep8_decode", "tp8", "ep8_prefill", "contiguous", "masked", "ep8_mid",
+                   "ep128_decode")
 FLUSH_BYTES = 512 << 20
 
 DESCRIPTIONS = {
