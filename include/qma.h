@@ -87,9 +87,11 @@ typedef struct qma_layer qma_layer_t;
 
 /* GEMM kernel families the planner chooses between. */
 typedef enum qma_kernel {
-  /* Few rows per expert (decode): dequantised weights occupy the MFMA row
-   * side and tokens the 16-wide column side ([announce] scheduling section:
-   * decode swaps the MMA operands). HBM-bound. */
+  /* Few rows per expert (decode, up to 79): 16-, 32- or 64-row token
+   * tiles on the MFMA row side and weight columns on the column side, one
+   * 16x16x32 MFMA per scale group. (The pages' decode kernel swaps the
+   * operands because its MMA is 16 x 8, [announce] scheduling section; the
+   * 16 x 16 shapes of CDNA4 need no swap.) HBM-bound; takes split-K. */
   QMA_KERNEL_SMALL_M = 1,
   /* Many rows per expert (prefill): token tiles staged in LDS, weights
    * dequantised into the MFMA column side. MFMA-bound. Every wave loads,
@@ -204,11 +206,13 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * experts. tok_e = T*topk/E picks block_m ([release] indexed techniques: a
  * block-M heuristic keyed on routed tokens per expert, switching at 80),
  * block_n comes from the tile count ([release] grouped techniques: the
- * wider tile only when enough N tiles exist), and split-K turns on only
- * when the grid would underfill the compute units ([release] indexed
- * techniques: the stream-K gate). Between one and two workgroups per compute
- * unit with long K, 16-row tiles split K across wave pairs inside the
- * workgroup (waves_k = 2) instead. force_block_m = 0 lets the planner choose;
+ * wider tile only when enough N tiles exist, never below 128 columns with
+ * long K), and split-K turns on only when the grid would underfill the
+ * compute units ([release] indexed techniques: the stream-K gate); it then
+ * aims at 1.5 workgroups per compute unit and keeps at least 14 K chunks
+ * of 128 per split. Between one and two workgroups per compute unit with
+ * long K, 16-row tiles split K across wave pairs inside the workgroup
+ * (waves_k = 2) instead. force_block_m = 0 lets the planner choose;
  * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128
  * the large-M kernel (which needs N % 256 == 0). The down projection passes
  * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,
