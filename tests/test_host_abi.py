@@ -329,7 +329,7 @@ def test_planner_invariants_over_shapes():
     # every plan the planner returns names an existing kernel instance and
     # follows the documented rules, over a grid of layer and batch shapes
     import itertools
-    for E, N, K, T, topk in itertools.product((1, 8, 48, 384), (256, 512, 4096, 7168),
+    for E, N, K, T, topk in itertools.product((1, 8, 48, 384), (80, 256, 512, 1040, 4096, 7168),
                                               (256, 2048, 7168), (1, 17, 256, 8192), (1, 8)):
         lay = qma.qma_layer_create(E, N, K)
         try:
