@@ -348,6 +348,15 @@ qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
   L.profile = infer_profile(E, N, K);
   L.n_tiles = N / qma::kTileN;
   L.k_chunks = K / qma::kChunkK;
+  // one expert's packed weights are addressed with 32-bit offsets
+  if ((int64_t)L.n_tiles * L.k_chunks * qma::kWBlockBytes >= (1ll << 31)) {
+    delete l;
+    return fail(QMA_ERR_INVALID_ARG, "N=%d x K=%d: one expert's packed weights exceed 2 GiB", N, K);
+  }
+  L.wg_log2 = ((L.profile == QMA_PROFILE_EP_GATE_UP || L.profile == QMA_PROFILE_TP_GATE_UP) &&
+               L.n_tiles % (1 << qma::kGateUpGroupLog2) == 0)
+                  ? qma::kGateUpGroupLog2
+                  : 0;
   L.w_bytes = (size_t)E * L.n_tiles * L.k_chunks * qma::kWBlockBytes;
   L.s_bytes = (size_t)E * L.n_tiles * L.k_chunks * qma::kSBlockBytes;
   *out = l;

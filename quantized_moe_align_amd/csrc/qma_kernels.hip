@@ -215,18 +215,29 @@ __device__ __forceinline__ uint32_t interleave_nibbles(uint32_t w) {
   return r;
 }
 
+// Output block number b (of 1 KiB weights or 128-byte scales) -> expert,
+// tile and K chunk, in the block order of the packed layout.
+__device__ __forceinline__ void block_place(int64_t b, int64_t n_tiles, int64_t k_chunks,
+                                            int wg_log2, int64_t& e, int64_t& nt, int64_t& kc) {
+  const int64_t g = (int64_t)1 << wg_log2;
+  const int64_t r = b & (g - 1);
+  int64_t rest = b >> wg_log2;
+  kc = rest % k_chunks;
+  rest /= k_chunks;
+  const int64_t groups = n_tiles >> wg_log2;
+  nt = (rest % groups) * g + r;
+  e = rest / groups;
+}
+
 __global__ void prepack_weights_kernel(const uint32_t* __restrict__ qw, uint32_t* __restrict__ out,
                                        int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
-                                       int64_t total) {
+                                       int32_t wg_log2, int64_t total) {
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
     const int j = (int)(o & 3);
     const int l = (int)((o >> 2) & 63);
-    int64_t rest = o >> 8;
-    const int64_t kc = rest % k_chunks;
-    rest /= k_chunks;
-    const int64_t nt = rest % n_tiles;
-    const int64_t e = rest / n_tiles;
+    int64_t e, nt, kc;
+    block_place(o >> 8, n_tiles, k_chunks, wg_log2, e, nt, kc);
     const int64_t n = nt * 16 + (l & 15);
     const int64_t k0 = kc * 128 + j * 32 + (l >> 4) * 8;
     out[o] = interleave_nibbles(qw[(e * N + n) * (K / 8) + k0 / 8]);
@@ -235,16 +246,13 @@ __global__ void prepack_weights_kernel(const uint32_t* __restrict__ qw, uint32_t
 
 __global__ void prepack_scales_kernel(const uint16_t* __restrict__ sc, uint16_t* __restrict__ out,
                                       int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
-                                      int64_t total) {
+                                      int32_t wg_log2, int64_t total) {
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
     const int g = (int)(o & 3);
     const int row = (int)((o >> 2) & 15);
-    int64_t rest = o >> 6;
-    const int64_t kc = rest % k_chunks;
-    rest /= k_chunks;
-    const int64_t nt = rest % n_tiles;
-    const int64_t e = rest / n_tiles;
+    int64_t e, nt, kc;
+    block_place(o >> 6, n_tiles, k_chunks, wg_log2, e, nt, kc);
     const int64_t n = nt * 16 + row;
     out[o] = sc[(e * N + n) * (K / 32) + kc * 4 + g];
   }
@@ -257,10 +265,10 @@ int launch_prepack(const Layer& L, const int32_t* qweight, const uint16_t* scale
   auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
   hipLaunchKernelGGL(prepack_weights_kernel, dim3(blocks(words)), dim3(256), 0,
                      (hipStream_t)stream, (const uint32_t*)qweight, (uint32_t*)packed, L.N, L.K,
-                     L.n_tiles, L.k_chunks, words);
+                     L.n_tiles, L.k_chunks, L.wg_log2, words);
   hipLaunchKernelGGL(prepack_scales_kernel, dim3(blocks(svals)), dim3(256), 0,
                      (hipStream_t)stream, scales, (uint16_t*)((char*)packed + L.w_bytes), L.N,
-                     L.K, L.n_tiles, L.k_chunks, svals);
+                     L.K, L.n_tiles, L.k_chunks, L.wg_log2, svals);
   return (int)hipGetLastError();
 }
 
@@ -308,7 +316,23 @@ struct GemmParams {
   int32_t E, N, K, NT, KC, BM;
   int32_t nstream, nbtot;  // streaming small-M: N blocks per workgroup, N blocks in all
   int32_t* work;            // dynamic schedule: work counter (workspace)
+  int32_t wg_log2;          // packed layout: log2 of the tiles per block group
 };
+
+// Place of 16-column tile t0 + j, K chunk c inside one expert's packed
+// weights or scales (unit = the block size, kWBlockBytes or kSBlockBytes):
+// byte offset base + j * tile + c * chunk, for j within t0's tile group
+// (callers keep a wave's tiles inside one group: group sizes are 1 or 16,
+// and each wave's first tile is a multiple of its tile count).
+struct TileAddr {
+  uint32_t base, tile, chunk;
+};
+__device__ __forceinline__ TileAddr tile_addr(const GemmParams& p, int t0, uint32_t unit) {
+  const int lg = p.wg_log2;
+  const uint32_t g = 1u << lg;
+  const uint32_t grp = (uint32_t)t0 >> lg, r = (uint32_t)t0 & (g - 1);
+  return {(grp * (uint32_t)p.KC * g + r) * unit, (lg ? 1u : (uint32_t)p.KC) * unit, g * unit};
+}
 
 struct RowInfo {
   bool valid;
@@ -542,13 +566,14 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   const int nt0 = (nb * WN + wn) * NTW;  // first 16-column tile of this wave
   const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
   const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, NTW * tile_bytes);
+      make_rsrc(p.wpk + (size_t)e * p.NT * tile_bytes, (uint32_t)p.NT * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * p.KC * kSBlockBytes,
-                NTW * p.KC * kSBlockBytes);
+      make_rsrc(p.spk + (size_t)e * p.NT * p.KC * kSBlockBytes,
+                (uint32_t)p.NT * p.KC * kSBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-  const uint32_t voff_w = lane * 16;
-  const uint32_t voff_s = col * 8;
+  const TileAddr wa = tile_addr(p, nt0, kWBlockBytes), sa = tile_addr(p, nt0, kSBlockBytes);
+  const uint32_t voff_w = lane * 16 + wa.base;
+  const uint32_t voff_s = col * 8 + sa.base;
   uint32_t voff_x[TM];
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
@@ -566,11 +591,11 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   auto load = [&](Stage& s, int c) {
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, nt * tile_bytes + c * kWBlockBytes,
+      s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, nt * wa.tile + c * wa.chunk,
                                                       kNonTemporal);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, (nt * p.KC + c) * kSBlockBytes, 0);
+      s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, nt * sa.tile + c * sa.chunk, 0);
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm)
 #pragma unroll
@@ -772,8 +797,8 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   const __amdgpu_buffer_rsrc_t rs =
       make_rsrc(p.spk + (size_t)e * p.NT * KC * kSBlockBytes, (uint32_t)p.NT * KC * kSBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-  const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
-  const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
+  const uint32_t voff_w = lane * 16;
+  const uint32_t voff_s = col * 8;
   const RowInfo rx = row_info(p, tile, e, col);
   const uint32_t voff_x = rx.valid ? (uint32_t)rx.a_row * (uint32_t)p.K * 2u + kb * 16 : 0x80000000u;
   int32_t out_row[4];
@@ -794,15 +819,17 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   // load cursor: column block and chunk of the next stage to fetch
   int l_nb = nb0, l_c = 0;
   auto load_next = [&](Stage& s) {
-    const int t0 = l_nb * 4 * NTW;
+    // this wave's tiles of column block l_nb: (l_nb * 4 + w) * NTW + nt
+    const int t0 = (l_nb * 4 + w) * NTW;
+    const TileAddr wa = tile_addr(p, t0, kWBlockBytes), sa = tile_addr(p, t0, kSBlockBytes);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
       s.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
-          rw, voff_w, (t0 + nt) * tile_bytes + l_c * kWBlockBytes, kNonTemporal);
+          rw, voff_w, wa.base + nt * wa.tile + l_c * wa.chunk, kNonTemporal);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
       s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
-                                                     ((t0 + nt) * KC + l_c) * kSBlockBytes, 0);
+                                                     sa.base + nt * sa.tile + l_c * sa.chunk, 0);
 #pragma unroll
     for (int g = 0; g < 4; ++g)
       s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
@@ -965,13 +992,14 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   const int nt0 = nb * 4 * NTW;
   const uint32_t tile_bytes = (uint32_t)KC * kWBlockBytes;
   const __amdgpu_buffer_rsrc_t rw =
-      make_rsrc(p.wpk + ((size_t)e * p.NT + nt0) * tile_bytes, 4u * NTW * tile_bytes);
+      make_rsrc(p.wpk + (size_t)e * p.NT * tile_bytes, (uint32_t)p.NT * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(p.spk + ((size_t)e * p.NT + nt0) * KC * kSBlockBytes,
-                4u * NTW * KC * kSBlockBytes);
+      make_rsrc(p.spk + (size_t)e * p.NT * KC * kSBlockBytes, (uint32_t)p.NT * KC * kSBlockBytes);
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
-  const uint32_t voff_w = lane * 16 + (uint32_t)(w * NTW) * tile_bytes;
-  const uint32_t voff_s = col * 8 + (uint32_t)(w * NTW * KC) * kSBlockBytes;
+  const TileAddr wa = tile_addr(p, nt0 + w * NTW, kWBlockBytes);
+  const TileAddr sa = tile_addr(p, nt0 + w * NTW, kSBlockBytes);
+  const uint32_t voff_w = lane * 16 + wa.base;
+  const uint32_t voff_s = col * 8 + sa.base;
   // wave w copies rows 4 (w * NX + i) + l / 16, i < NX
   uint32_t voff_x[NX];
 #pragma unroll
@@ -1006,12 +1034,11 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
     const int c = chunk(f);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w,
-                                                       nt * tile_bytes + c * kWBlockBytes,
+      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(rw, voff_w, nt * wa.tile + c * wa.chunk,
                                                        kNonTemporal);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
-      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, (nt * KC + c) * kSBlockBytes, 0);
+      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, nt * sa.tile + c * sa.chunk, 0);
   };
   auto load_x = [&](auto buf_id, int f) {
     constexpr int b = decltype(buf_id)::value;
@@ -1401,13 +1428,14 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
   const int nt16 = nb * (kLmBN / 16) + w * 4;
   const uint32_t tile_bytes = (uint32_t)p.KC * kWBlockBytes;
   const __amdgpu_buffer_rsrc_t rw = make_rsrc(
-      uniform_ptr(p.wpk + ((size_t)e * p.NT + nt16) * tile_bytes), 4 * tile_bytes);
+      uniform_ptr(p.wpk + (size_t)e * p.NT * tile_bytes), (uint32_t)p.NT * tile_bytes);
   const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(uniform_ptr(p.spk + ((size_t)e * p.NT + nt16) * p.KC * kSBlockBytes),
-                4 * p.KC * kSBlockBytes);
+      make_rsrc(uniform_ptr(p.spk + (size_t)e * p.NT * p.KC * kSBlockBytes),
+                (uint32_t)p.NT * p.KC * kSBlockBytes);
+  const TileAddr wa = tile_addr(p, nt16, kWBlockBytes), sa = tile_addr(p, nt16, kSBlockBytes);
   const int half16 = (lane >> 4) & 1;  // which 16-column tile of the 32
-  const uint32_t voff_w = half16 * tile_bytes + (uint32_t)(c16 + 16 * kq) * 16u;
-  const uint32_t voff_s = half16 * p.KC * kSBlockBytes + c16 * 8;
+  const uint32_t voff_w = wa.base + half16 * wa.tile + (uint32_t)(c16 + 16 * kq) * 16u;
+  const uint32_t voff_s = sa.base + half16 * sa.tile + c16 * 8;
   const __amdgpu_buffer_rsrc_t ra = make_rsrc(uniform_ptr(p.a), p.a_bytes);
 
   // The main loop and epilogue for a tile whose valid rows lie in its first
@@ -1462,11 +1490,10 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
 #pragma unroll
         for (int h = 0; h < 2; ++h)
           b.w[t][h] = __builtin_amdgcn_raw_buffer_load_b128(
-              rw, voff_w, 2 * t * tile_bytes + c * kWBlockBytes + h * 512, 0);
+              rw, voff_w, 2 * t * wa.tile + c * wa.chunk + h * 512, 0);
 #pragma unroll
       for (int t = 0; t < kLmNT; ++t)
-        b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
-                                                      (2 * t * p.KC + c) * kSBlockBytes, 0);
+        b.s[t] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s, 2 * t * sa.tile + c * sa.chunk, 0);
     };
 
     f32x16 acc[MT][kLmNT];
@@ -1856,7 +1883,7 @@ __device__ __forceinline__ void pc_producer(const GemmParams& p, const PcWalk& w
   // weights: ring of three chunks of this producer's two 16-column tiles
   u32x4 wv[3][2];
   u32x2 sv[3][2];
-  int w_item = -1;
+  int w_item = -1, wt0 = 0;
   const uint8_t* wbase = p.wpk;
   const uint8_t* sbase = p.spk;
   auto load_w = [&](auto ring_c, int u) __attribute__((always_inline)) {
@@ -1866,21 +1893,25 @@ __device__ __forceinline__ void pc_producer(const GemmParams& p, const PcWalk& w
     if (i != w_item) {
       int tile, nb, e;
       wk.item(p, i, tile, nb, e);
-      const size_t t0 = (size_t)max(e, 0) * p.NT + (size_t)nb * (kLmBN / 16) + pw * 2;
-      wbase = p.wpk + t0 * tile_bytes;
-      sbase = p.spk + t0 * (size_t)KC * kSBlockBytes;
+      const size_t ex = (size_t)max(e, 0) * p.NT;
+      wbase = p.wpk + ex * tile_bytes;
+      sbase = p.spk + ex * (size_t)KC * kSBlockBytes;
+      wt0 = nb * (kLmBN / 16) + pw * 2;
       w_item = i;
     }
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(uniform_ptr(wbase), 2 * tile_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(uniform_ptr(wbase), (uint32_t)p.NT * tile_bytes);
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(uniform_ptr(sbase), 2 * (uint32_t)KC * kSBlockBytes);
+        make_rsrc(uniform_ptr(sbase), (uint32_t)p.NT * KC * kSBlockBytes);
+    const TileAddr wa = tile_addr(p, wt0, kWBlockBytes), sa = tile_addr(p, wt0, kSBlockBytes);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      wv[r][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16, t * tile_bytes + c * kWBlockBytes,
+      wv[r][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, lane * 16,
+                                                       wa.base + t * wa.tile + c * wa.chunk,
                                                        kNonTemporal);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-      sv[r][t] = __builtin_amdgcn_raw_buffer_load_b64(rs, c16 * 8, (t * KC + c) * kSBlockBytes, 0);
+      sv[r][t] = __builtin_amdgcn_raw_buffer_load_b64(rs, c16 * 8,
+                                                      sa.base + t * sa.tile + c * sa.chunk, 0);
   };
   // dequantise quarter j (word j, scale group j) of the chunk in ring slot
   // r into weight buffer b: this producer's 32-column tile ct = pw, K step
@@ -2172,6 +2203,7 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   gp.NT = (int32_t)L.n_tiles;
   gp.KC = (int32_t)L.k_chunks;
   gp.BM = pl.block_m;
+  gp.wg_log2 = L.wg_log2;
   const int64_t tiles_pad = (g.num_tiles + 7) / 8 * 8;
   const int64_t grid = tiles_pad * gp.nblocks * gp.split;
   if (grid <= 0) return 0;
