@@ -61,6 +61,16 @@ def test_bad_shapes(L, E, N, K):
     assert ei.value.status == qma.QMA_ERR_INVALID_ARG
 
 
+def test_per_expert_weights_must_fit_32_bit_offsets(L):
+    # kernels address one expert's packed blocks with 32-bit offsets: N x K / 2
+    # bytes of nibbles must stay below 2 GiB (65536 x 65536 / 2 = 2 GiB exactly)
+    with pytest.raises(qma.QmaError) as ei:
+        qma.qma_layer_create(1, 65536, 65536)
+    assert ei.value.status == qma.QMA_ERR_INVALID_ARG and "2 GiB" in ei.value.detail
+    lay = qma.qma_layer_create(1, 65536 - 16, 65536)      # one tile less fits
+    qma.qma_layer_destroy(lay)
+
+
 def test_null_out_pointer(L):
     d = qma.w4a16_desc()
     assert L.qma_layer_create(ctypes.byref(d), 8, 256, 256, 0, None) == qma.QMA_ERR_INVALID_ARG
