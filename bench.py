@@ -405,8 +405,10 @@ def build_runner(name, seed, cache, schedule, overrides):
         stages = [("gate_up", lambda: moe.gate_up(a, index)), ("silu_and_mul", moe.act),
                   ("down", lambda: moe.down(index))]
     applied = (False, False)
-    if schedule == "dynamic":
-        applied = moe.set_schedule(qma.SCHEDULE_DYNAMIC)
+    if schedule != "planner":
+        applied = moe.set_schedule({"semi_static": qma.SCHEDULE_SEMI_STATIC,
+                                    "dynamic": qma.SCHEDULE_DYNAMIC,
+                                    "gang": qma.SCHEDULE_GANG}[schedule])
     for which, ov in (("13", overrides.get("gate_up")), ("2", overrides.get("down"))):
         if ov:
             plan = getattr(moe, "plan" + which)
@@ -539,10 +541,12 @@ def main():
                     help="seconds of oracle CPU work for cpu_baseline (0 = skip the CPU legs)")
     ap.add_argument("--cpu-fp32-experts", type=int, default=4,
                     help="experts in the fp32 NumPy legs of cpu_baseline")
-    ap.add_argument("--schedule", default="semi_static", choices=("semi_static", "dynamic"),
-                    help="how small-M GEMMs hand out (tile, column block) work; dynamic "
-                         "applies where the plan accepts it (16/32-row tiles, one K "
-                         "partition)")
+    ap.add_argument("--schedule", default="planner",
+                    choices=("planner", "semi_static", "dynamic", "gang"),
+                    help="how small-M GEMMs hand out (tile, column block) work: the "
+                         "planner's choice, or one schedule forced where the plan accepts "
+                         "it (dynamic: 16/32-row tiles, one K partition; gang: the "
+                         "shared-row instances)")
     ap.add_argument("--override-gate-up", default="",
                     help="JSON object of plan fields to set on the headline workload's "
                          "gate_up plan before timing (A/B runs, e.g. '{\"split_k\": 1}')")
@@ -616,7 +620,8 @@ def main():
                 "unit": "TFLOP/s", "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4)}
     roof["traffic"] = traffic["gate_up"]
     roof["kernel"] = "gate_up GEMM (" + ("small-M" if moe.plan13.kernel == 1 else "large-M") + ")"
-    sched = r["schedule"]
+    sched = {"gate_up": qma.SCHEDULE_NAMES.get(moe.plan13.schedule, "?"),
+             "down": qma.SCHEDULE_NAMES.get(moe.plan2.schedule, "?")}
     headline_plan = {"gate_up": moe.plan13.as_dict(), "down": moe.plan2.as_dict()}
     wl_main = r["wl"]
     del r, moe
@@ -630,8 +635,7 @@ def main():
         "config": {"workload": DESCRIPTIONS[args.workload], "name": args.workload,
                    "rows": work["rows"], "weights": "uint4 group-32 bf16 scales, zero point 8",
                    "parallelism": "one EP/TP rank's share on one GPU",
-                   "schedule": {"gate_up": "dynamic" if sched[0] else "semi_static",
-                                "down": "dynamic" if sched[1] else "semi_static"},
+                   "schedule": sched,
                    **({"plan_overrides": overrides} if any(overrides.values()) else {}),
                    **({"idle_gap_ms": args.idle_gap_ms} if args.idle_gap_ms > 0 else {})},
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
@@ -652,7 +656,7 @@ def main():
     if configs:
         cfg_out = {}
         for name in configs:
-            rc = build_runner(name, args.seed, cache, "semi_static", {})
+            rc = build_runner(name, args.seed, cache, "planner", {})
             mc = measure(rc, args.steps, args.warmup, min(args.settle_ms, 150.0), flush=flush)
             rep = pair_report(name, rc["work"], mc["ev"], read_traffic(name))
             rep["ms_per_step"] = round(mc["ms_per_step"], 4)

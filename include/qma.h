@@ -153,16 +153,31 @@ typedef struct qma_plan {
  *   SEMI_STATIC: the grid is sized from host-known shapes and each
  *     workgroup derives its tile, expert and rows from the routing buffers
  *     on the device; workgroups past num_tokens_padded exit at once. The
- *     planner's default.
+ *     planner's default, except where it picks GANG.
  *   DYNAMIC: a persistent grid (three workgroups per CU) whose workgroups
  *     take items from a device work counter until the routed items run
  *     out. The counter lives in the workspace (qma_workspace_bytes counts
  *     it) and is reset by a one-thread kernel on the same stream before the
  *     GEMM. Only 16/32-row tiles with one K partition, no split-K and
- *     n_stream = 1 accept it; other plans -> QMA_ERR_INVALID_ARG. */
+ *     n_stream = 1 accept it; other plans -> QMA_ERR_INVALID_ARG.
+ *   GANG: the semi-static item order, run by one workgroup per CU holding
+ *     three groups of four waves, each group on its own (tile, column
+ *     block, split) item. The groups share one barrier per K chunk, so the
+ *     items on a CU advance together and end together, where separate
+ *     workgroups would end staggered and leave the CU streaming with few
+ *     loads in flight. Items beyond one round loop in the same order. The
+ *     planner picks it for shared-row plans with one K partition and at
+ *     least 8 K chunks whose items fill one such round: at least 5/6 of the
+ *     3 x 256 slots, and at most the 3 x 32 slots of an XCD on the fullest
+ *     XCD (token tiles are dealt to the 8 XCDs in turn), trying the plan's
+ *     width, then 256, then 128 columns. Accepted for waves_k = 1,
+ *     n_stream = 1, block_n 128 or 256 and block_m 16, 32 or 64 (the
+ *     shared-row instances), with or without split-K; other plans ->
+ *     QMA_ERR_INVALID_ARG. No workspace beyond split-K's. */
 typedef enum {
   QMA_SCHEDULE_SEMI_STATIC = 0,
-  QMA_SCHEDULE_DYNAMIC = 1
+  QMA_SCHEDULE_DYNAMIC = 1,
+  QMA_SCHEDULE_GANG = 2
 } qma_schedule;
 
 /* ---- layer (load time) ------------------------------------------------ */
@@ -212,7 +227,9 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * aims at 1.5 workgroups per compute unit and keeps at least 14 K chunks
  * of 128 per split. Between one and two workgroups per compute unit with
  * long K, 16-row tiles split K across wave pairs inside the workgroup
- * (waves_k = 2) instead. force_block_m = 0 lets the planner choose;
+ * (waves_k = 2) instead. Plans whose items fill one round of the gang
+ * schedule take it (QMA_SCHEDULE_GANG, with its width rule); the others
+ * are semi-static. force_block_m = 0 lets the planner choose;
  * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128
  * the large-M kernel (which needs N % 256 == 0). The down projection passes
  * gate_up's block_m so one moe_align serves both. Errors: T < 0, topk < 1,

@@ -164,6 +164,32 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     while (ns > 1 && (int64_t)tiles_m * ceil_div(nblocks, ns) < 4 * qma::kNumCUs) --ns;
     p->n_stream = std::max<int32_t>(ns, 1);
   }
+  // Gang schedule: where the items of a shared-row plan fill one round of
+  // kGangGroups lock-step groups on every CU (5/6 of the slots or more),
+  // at this width or the other one, each CU runs one workgroup holding all
+  // of its items. As separate workgroups they end staggered: on the EP8
+  // decode gate_up share the three on a CU ran 84, 104 and 120 us, and the
+  // CU streamed at 57 % of its full rate once one was left. Measured, same
+  // box: EP8 decode gate_up 127-129 -> 119-121 us, TP8 gate_up (256
+  // columns) 129-130 -> 121-122 us, masked gate_up 157 -> 149-152 us.
+  p->schedule = QMA_SCHEDULE_SEMI_STATIC;
+  if (wk == 1 && split == 1 && p->n_stream == 1 && L.k_chunks >= qma::kStreamChunks) {
+    const int64_t slots = (int64_t)qma::kGangGroups * qma::kNumCUs;
+    for (const int cand : {ntw, 4, 2}) {
+      if (!qma::small_m_shared_rows(tm, cand, 1) || L.N % (64 * cand) != 0) continue;
+      // token tiles are dealt to the 8 XCDs in turn, all column blocks of a
+      // tile on one XCD: the fullest XCD must fit one round too (an EP32
+      // down share, 12 tiles x 56 blocks, has 112 items on four XCDs and ran
+      // 40.9 us this way against 28.6 us semi-static)
+      const int64_t items = (int64_t)tiles_m * (L.N / (64 * cand));
+      const int64_t per_xcd = ceil_div(tiles_m, 8) * (int64_t)(L.N / (64 * cand));
+      if (per_xcd > slots / 8 || 6 * items < qma::kGangMinFill * slots) continue;
+      p->block_n = 64 * cand;
+      p->est_tiles = (int32_t)items;
+      p->schedule = QMA_SCHEDULE_GANG;
+      break;
+    }
+  }
 }
 
 // Large-M kernel: 128-token tiles, 256 columns per workgroup.
@@ -247,7 +273,12 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
   if (plan->split_k > L.k_chunks)
     return fail(QMA_ERR_INVALID_ARG, "split_k %d exceeds the %lld K chunks of 128", plan->split_k,
                 (long long)L.k_chunks);
+  const bool gang_ok =
+      plan->kernel == QMA_KERNEL_SMALL_M && plan->waves_k == 1 && plan->n_stream == 1 &&
+      (plan->block_n == 128 || plan->block_n == 256) && plan->block_m % 16 == 0 &&
+      qma::small_m_shared_rows(plan->block_m / 16, plan->block_n / 64, 1);
   if (plan->schedule != QMA_SCHEDULE_SEMI_STATIC &&
+      !(plan->schedule == QMA_SCHEDULE_GANG && gang_ok) &&
       (plan->schedule != QMA_SCHEDULE_DYNAMIC || plan->kernel != QMA_KERNEL_SMALL_M ||
        plan->waves_k != 1 || plan->split_k != 1 || plan->n_stream != 1 ||
        (plan->block_m != 16 && plan->block_m != 32) ||

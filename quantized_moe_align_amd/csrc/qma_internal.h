@@ -44,6 +44,12 @@ constexpr int kStreamTargetChunks = 14;
 // shorter run pays the pipeline's start and the reduction for too little
 // streaming
 constexpr int kSplitChunks = 14;
+constexpr int kLdsPerCU = 160 * 1024;
+// Gang schedule: four-wave groups per workgroup, one workgroup per CU. The
+// planner takes it for a shared-row GEMM whose planned items fill between
+// kGangMinFill sixths and all of one round of kGangGroups * kNumCUs slots.
+constexpr int kGangGroups = 3;
+constexpr int kGangMinFill = 5;
 // bytes at the end of the workspace holding a dynamic schedule's counter
 constexpr int kWorkCounterBytes = 256;
 // size of the library's static device scratch (qma_indexed_gemm_scratch):

@@ -507,8 +507,8 @@ __device__ __forceinline__ void wait_lgkm(u32x4& v) {
 // XCD x takes token tiles x, x+8, ... with all of their (column block,
 // split) pieces. A tile's activations then stay in one XCD's L2, and empty
 // tiles spread evenly over the XCDs.
-__device__ __forceinline__ bool decode_bid(const GemmParams& p, int& tile, int& nb, int& sp) {
-  const int bid = blockIdx.x;
+__device__ __forceinline__ bool decode_bid(const GemmParams& p, int bid, int& tile, int& nb,
+                                           int& sp) {
   const int xcd = bid & 7;
   const int idx = bid >> 3;
   const int per_tile = p.nblocks * p.split;
@@ -549,7 +549,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   __shared__ float s_red[WK > 1 ? 4 * NACC * 64 : 1];
 
   int tile, nb, sp;
-  if (!decode_bid(p, tile, nb, sp)) return;
+  if (!decode_bid(p, blockIdx.x, tile, nb, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
   if (e < 0) return;
 
@@ -778,7 +778,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
 template <int NTW, int D>
 __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmParams p) {
   int tile, grp, sp;
-  if (!decode_bid(p, tile, grp, sp)) return;
+  if (!decode_bid(p, blockIdx.x, tile, grp, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
   if (e < 0) return;
 
@@ -968,7 +968,7 @@ constexpr int xs_lds_bytes() { return D * TM * 16 * 256 + TM * 16 * 8; }
 // tile's output rows and topk weights (TM * 16 of each).
 template <int TM, int NTW, int D>
 __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, int sp,
-                                        uint8_t* s_x) {
+                                        uint8_t* s_x, int tid) {
   constexpr int XROW = 256;
   constexpr int XBUF = TM * 16 * XROW;       // one chunk of the tile's token rows
   constexpr int NX = TM;                     // direct-to-LDS loads per wave and chunk
@@ -977,8 +977,8 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
   if (e < 0) return;
 
-  const int lane = threadIdx.x & 63;
-  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kb = lane >> 4;
   const int KC = p.KC;
   // this workgroup's K range (all of K without split-K; the host keeps
@@ -1252,8 +1252,8 @@ __global__ __launch_bounds__(256, (xs_occupancy<TM, NTW>())) void gemm_small_m_x
     const GemmParams p) {
   __shared__ __attribute__((aligned(1024))) uint8_t s_x[xs_lds_bytes<TM, D>()];
   int tile, grp, sp;
-  if (!decode_bid(p, tile, grp, sp)) return;
-  xs_tile<TM, NTW, D>(p, tile, grp, sp, s_x);
+  if (!decode_bid(p, blockIdx.x, tile, grp, sp)) return;
+  xs_tile<TM, NTW, D>(p, tile, grp, sp, s_x, (int)threadIdx.x);
 }
 
 // Dynamic schedule: a persistent grid whose workgroups take (tile, column
@@ -1270,8 +1270,35 @@ __global__ __launch_bounds__(256, 3) void gemm_small_m_xs_dyn_kernel(const GemmP
     const int it = __builtin_amdgcn_readfirstlane(s_item);
     if (it >= items) break;
     const int tile = it / p.nblocks;
-    xs_tile<TM, NTW, D>(p, tile, it - tile * p.nblocks, 0, s_x);
+    xs_tile<TM, NTW, D>(p, tile, it - tile * p.nblocks, 0, s_x, (int)threadIdx.x);
     // every wave is done with s_item and the LDS ring before the next item
+    __syncthreads();
+  }
+}
+
+// Gang schedule: a persistent grid whose workgroups hold S groups of four
+// waves, each group running its own (tile, column block, split) item. The
+// groups share the per-chunk barrier, so the items of a workgroup advance in
+// lock-step and end together. Separate workgroups on one CU do not: the
+// oldest is issued first and finishes early, and the CU then streams with
+// fewer loads in flight. Items keep the XCD-aware order: group g of
+// workgroup b takes the items k = (b / 8) * S + g, then k + S * grid / 8,
+// ... of XCD b % 8.
+template <int TM, int D>
+constexpr int xs_gang_stride() { return (xs_lds_bytes<TM, D>() + 1023) / 1024 * 1024; }
+
+template <int TM, int NTW, int D, int S>
+__global__ __launch_bounds__(256 * S, 1) void gemm_small_m_xs_gang_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t s_x[S * xs_gang_stride<TM, D>()];
+  const int g = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
+  const int tid = (int)(threadIdx.x & 255);
+  const int xcd = blockIdx.x & 7;
+  const int step = (int)(gridDim.x >> 3) * S;
+  for (int k = (int)(blockIdx.x >> 3) * S + g;; k += step) {
+    int tile, nb, sp;
+    if (!decode_bid(p, k * 8 + xcd, tile, nb, sp)) break;
+    xs_tile<TM, NTW, D>(p, tile, nb, sp, s_x + g * xs_gang_stride<TM, D>(), tid);
+    // the group's LDS ring and row table are free for its next item
     __syncthreads();
   }
 }
@@ -2170,6 +2197,22 @@ static int launch_small_m_wk(const GemmParams& gp, unsigned grid, hipStream_t st
   return (int)hipErrorInvalidConfiguration;
 }
 
+// Gang schedule: one workgroup of kGangGroups groups per CU. The launch asks
+// for enough LDS that a second workgroup never fits beside the first, so
+// every CU runs its groups in lock-step to the end.
+template <int TM, int NTW>
+static int launch_xs_gang(const GemmParams& gp, int64_t items, hipStream_t st) {
+  constexpr int S = kGangGroups;
+  constexpr size_t stat = (size_t)S * xs_gang_stride<TM, 2>();
+  constexpr size_t one_per_cu = kLdsPerCU / 2 + 1024;
+  const size_t dyn = stat < one_per_cu ? one_per_cu - stat : 0;
+  const int64_t need = (items + 8 * S - 1) / (8 * S) * 8;
+  const unsigned grid = (unsigned)std::min<int64_t>(kNumCUs, need);
+  hipLaunchKernelGGL((gemm_small_m_xs_gang_kernel<TM, NTW, 2, S>), dim3(grid), dim3(256 * S),
+                     dyn, st, gp);
+  return (int)hipGetLastError();
+}
+
 int launch_gemm(const GemmArgs& g, void* stream) {
   const Layer& L = *g.layer;
   const qma_plan_t& pl = *g.plan;
@@ -2264,21 +2307,35 @@ int launch_gemm(const GemmArgs& g, void* stream) {
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
     const dim3 sg((unsigned)(tiles_pad * gp.nblocks * gp.split));
-    if (xs && tm == 1 && ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 4, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs && tm == 1)
-      hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 2, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs && tm == 2 && ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 4, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs && tm == 2)
-      hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);
-    else if (xs)
-      hipLaunchKernelGGL((gemm_small_m_xs_kernel<4, 2, 2>), sg, dim3(256), 0, st, gp);
-    else if (ntw == 4)
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), sg, dim3(256), 0, st, gp);
-    else
-      hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), sg, dim3(256), 0, st, gp);
-    err = (int)hipGetLastError();
+    if (pl.schedule == QMA_SCHEDULE_GANG) {
+      if (!xs) return (int)hipErrorInvalidConfiguration;
+      if (tm == 1 && ntw == 4)
+        err = launch_xs_gang<1, 4>(gp, sg.x, st);
+      else if (tm == 1)
+        err = launch_xs_gang<1, 2>(gp, sg.x, st);
+      else if (tm == 2 && ntw == 4)
+        err = launch_xs_gang<2, 4>(gp, sg.x, st);
+      else if (tm == 2)
+        err = launch_xs_gang<2, 2>(gp, sg.x, st);
+      else
+        err = launch_xs_gang<4, 2>(gp, sg.x, st);
+    } else {
+      if (xs && tm == 1 && ntw == 4)
+        hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 4, 2>), sg, dim3(256), 0, st, gp);
+      else if (xs && tm == 1)
+        hipLaunchKernelGGL((gemm_small_m_xs_kernel<1, 2, 2>), sg, dim3(256), 0, st, gp);
+      else if (xs && tm == 2 && ntw == 4)
+        hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 4, 2>), sg, dim3(256), 0, st, gp);
+      else if (xs && tm == 2)
+        hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);
+      else if (xs)
+        hipLaunchKernelGGL((gemm_small_m_xs_kernel<4, 2, 2>), sg, dim3(256), 0, st, gp);
+      else if (ntw == 4)
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), sg, dim3(256), 0, st, gp);
+      else
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), sg, dim3(256), 0, st, gp);
+      err = (int)hipGetLastError();
+    }
   } else {
     if (!small_m_wave_rows(tm, ntw, wk) || ntw * 16 * (4 / wk) != pl.block_n)
       return (int)hipErrorInvalidConfiguration;

@@ -80,11 +80,22 @@ def workspace_for(plan: qma.Plan, device="cuda") -> Optional[torch.Tensor]:
     return torch.empty(n, dtype=torch.uint8, device=device) if n else None
 
 
-def schedule_applies(plan: qma.Plan) -> bool:
-    """Whether a plan can take the dynamic schedule (16/32-row small-M tiles
-    with one K partition, no split-K, no column-block streaming)."""
-    return (plan.kernel == qma.KERNEL_SMALL_M and plan.waves_k == 1 and plan.split_k == 1
-            and plan.n_stream == 1 and plan.block_m in (16, 32) and plan.block_n in (128, 256))
+def schedule_applies(plan: qma.Plan, schedule: int = qma.SCHEDULE_DYNAMIC) -> bool:
+    """Whether a plan can take `schedule`: semi-static always; dynamic for
+    16/32-row small-M tiles with one K partition, no split-K and no
+    column-block streaming; gang for the shared-row small-M instances (one K
+    partition per workgroup, 128 or 256 columns, 16/32/64-row tiles, with
+    or without split-K, no streaming)."""
+    if schedule == qma.SCHEDULE_SEMI_STATIC:
+        return True
+    shared = (plan.kernel == qma.KERNEL_SMALL_M and plan.waves_k == 1 and plan.n_stream == 1
+              and plan.block_n in (128, 256))
+    if schedule == qma.SCHEDULE_DYNAMIC:
+        return shared and plan.split_k == 1 and plan.block_m in (16, 32)
+    if schedule == qma.SCHEDULE_GANG:
+        return shared and (plan.block_m, plan.block_n) in ((16, 128), (16, 256), (32, 128),
+                                                           (32, 256), (64, 128))
+    return False
 
 
 @dataclass
@@ -136,7 +147,7 @@ class IndexedMoE:
         done = []
         for name in ("13", "2"):
             plan = getattr(self, "plan" + name)
-            ok = schedule == qma.SCHEDULE_SEMI_STATIC or schedule_applies(plan)
+            ok = schedule_applies(plan, schedule)
             if ok:
                 plan.schedule = schedule
                 setattr(self, "ws" + name, workspace_for(plan, self._dev))
@@ -206,7 +217,7 @@ class GroupedMoE:
         done = []
         for name in ("13", "2"):
             plan = getattr(self, "plan" + name)
-            ok = schedule == qma.SCHEDULE_SEMI_STATIC or schedule_applies(plan)
+            ok = schedule_applies(plan, schedule)
             if ok:
                 plan.schedule = schedule
                 setattr(self, "ws" + name, workspace_for(plan, self._dev))

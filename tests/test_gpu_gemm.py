@@ -24,6 +24,15 @@ def weights(rng, E, N, K, integer=False):
     return w, s
 
 
+def apply_override(plan, override):
+    """Set plan fields; an override that gives no schedule runs semi-static
+    (the shapes it sets need not take the planner's schedule)."""
+    if override:
+        plan.schedule = qma.SCHEDULE_SEMI_STATIC
+    for k, v in (override or {}).items():
+        setattr(plan, k, v)
+
+
 def indexed(a_bits, a_row_div, ids, w, s, *, T=None, topk=None, force_bm=0, override=None,
             extra_cap=0, junk_tail=False, topk_w=None, pre=None):
     """Run moe_align + one indexed GEMM through the ABI; return output bits."""
@@ -34,8 +43,7 @@ def indexed(a_bits, a_row_div, ids, w, s, *, T=None, topk=None, force_bm=0, over
     R = T * topk
     W = ExpertWeights(w, s)
     plan = qma.qma_plan_indexed(W.layer, T, topk, force_bm)
-    for k, v in (override or {}).items():
-        setattr(plan, k, v)
+    apply_override(plan, override)
     B = plan.block_m
     cap = qma.qma_align_sizes(T, topk, E, B)[0] + extra_cap
     sorted_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
@@ -220,8 +228,7 @@ def contiguous(a_bits, m_idx, w, s, override=None):
     W = ExpertWeights(w, s, qma.PATH_GROUPED_CONTIGUOUS)
     M = m_idx.size
     plan = qma.qma_plan_grouped(W.layer, M, 0)
-    for k, v in (override or {}).items():
-        setattr(plan, k, v)
+    apply_override(plan, override)
     c = torch.full((M, N), SENT, dtype=torch.int16, device="cuda")
     ws = workspace_for(plan)
     qma.qma_grouped_contiguous_gemm(W.layer, plan, to_device(a_bits), to_device(m_idx), M,
@@ -235,8 +242,7 @@ def masked(a_bits, masked_m, expected_m, w, s, override=None):
     Eb, Mb, K = a_bits.shape
     W = ExpertWeights(w, s, qma.PATH_GROUPED_MASKED)
     plan = qma.qma_plan_grouped(W.layer, Mb, expected_m)
-    for k, v in (override or {}).items():
-        setattr(plan, k, v)
+    apply_override(plan, override)
     c = torch.full((E, Mb, N), SENT, dtype=torch.int16, device="cuda")
     ws = workspace_for(plan)
     qma.qma_grouped_masked_gemm(W.layer, plan, to_device(a_bits), to_device(masked_m), Mb,
@@ -705,6 +711,77 @@ def test_dynamic_schedule_grouped(gpu):
     row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
     assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N), row_e.reshape(-1),
                       "dynamic masked")
+
+
+# Gang schedule (one workgroup of three lock-step groups per CU, each group on
+# its own item, looping over rounds of items) against the semi-static grid:
+# the same kernel body, so bit for bit the same outputs, and with
+# integer-exact inputs both equal the oracle. The shapes give more items than
+# one round of 3 x 256 groups (so groups loop), ragged expert counts, slots
+# routed off the rank, and split-K with its reduction.
+GANG_CASES = [(16, 128, 1), (16, 256, 1), (32, 256, 1), (32, 128, 1), (64, 128, 1),
+              (16, 256, 2), (32, 128, 3), (64, 128, 2)]
+
+
+@pytest.mark.parametrize("bm,bn,split", GANG_CASES)
+def test_gang_schedule_matches_semi_static(gpu, bm, bn, split):
+    E, T, topk, K, N = 37, 700, 2, 512, 2048
+    rng = np.random.default_rng(300 + bm + bn + split)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    ids[ids == 5] = 6                             # one expert with no rows
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": bm, "block_n": bn, "waves_k": 1,
+          "split_k": split, "n_stream": 1}
+    static, _ = indexed(a, topk, ids, w, s, force_bm=bm, override=ov)
+    gang, plan = indexed(a, topk, ids, w, s, force_bm=bm, junk_tail=(bm == 32),
+                         override=dict(ov, schedule=qma.SCHEDULE_GANG))
+    assert plan.schedule == qma.SCHEDULE_GANG
+    assert np.array_equal(gang, static)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(gang[valid], rne(ref[valid]))
+    assert np.all(gang[~valid] == SENT)
+
+
+def test_gang_schedule_grouped(gpu):
+    E, K, N = 23, 512, 1536
+    rng = np.random.default_rng(320)
+    w, s = weights(rng, E, N, K)
+    counts = [int(c) for c in rng.integers(0, 90, E)]
+    counts[3] = 0
+    wl = inputs.make_contiguous("c", 6, E, 0, K, N // 2, counts=counts, weights=False)
+    m_idx = wl["m_indices"]
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": 16, "block_n": 128, "waves_k": 1,
+          "split_k": 1, "n_stream": 1}
+    got = contiguous(wl["a"], m_idx, w, s, dict(ov, schedule=qma.SCHEDULE_GANG))
+    assert np.array_equal(got, contiguous(wl["a"], m_idx, w, s, ov))
+    assert_per_expert(got, O.grouped_contiguous(wl["a"], m_idx, w, s), m_idx, "gang contiguous")
+    Mb = 64
+    masked_m = rng.integers(0, Mb + 1, E).astype(np.int32)
+    masked_m[:3] = (0, 1, Mb)
+    am = inputs.bf16_normal(rng, (E, Mb, K))
+    for ovm in (dict(ov, block_m=32, block_n=256), dict(ov, block_m=64, split_k=2)):
+        got_m = masked(am, masked_m, 32, w, s, dict(ovm, schedule=qma.SCHEDULE_GANG))
+        assert np.array_equal(got_m, masked(am, masked_m, 32, w, s, ovm))
+        ref_m = O.grouped_masked(am, masked_m, w, s)
+        row_e = np.array([[e if r < masked_m[e] else -1 for r in range(Mb)] for e in range(E)])
+        assert_per_expert(got_m.reshape(E * Mb, N), ref_m.reshape(E * Mb, N),
+                          row_e.reshape(-1), "gang masked")
+        assert np.all(got_m[row_e < 0] == SENT)
+
+
+def test_gang_schedule_with_nothing_routed(gpu):
+    E, T, topk, K, N = 6, 50, 2, 1024, 512
+    rng = np.random.default_rng(330)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = np.full((T, topk), -1, np.int32)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=16,
+                        override={"block_n": 128, "waves_k": 1, "split_k": 1, "n_stream": 1,
+                                  "schedule": qma.SCHEDULE_GANG})
+    assert plan.schedule == qma.SCHEDULE_GANG
+    assert np.all(got == SENT)
 
 
 # ---- degenerate routing: nothing to compute --------------------------------

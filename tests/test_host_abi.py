@@ -105,9 +105,11 @@ def test_plan_decode_ep8():
     # 48 tiles x 16 blocks of 256 columns: one full round of three per CU
     assert p.block_n == 256 and p.waves_k == 1 and p.split_k == 1
     assert p.k_depth == 256                            # shared-row kernel: 2 chunks
+    assert p.schedule == qma.SCHEDULE_GANG and p.est_tiles == 768
     # EP16 share: at 256 columns only 384 workgroups, so 128 columns
     q = _plan(24, 4096, 7168, 288, 1)
     assert q.block_m == 16 and q.block_n == 128 and q.waves_k == 1
+    assert q.schedule == qma.SCHEDULE_GANG and q.est_tiles == 768
     assert p.tok_e_x100 == 1200 and p.rows == 576
     assert qma.qma_workspace_bytes(p) == 0
 
@@ -115,13 +117,15 @@ def test_plan_decode_ep8():
 def test_plan_tp8_and_tiny():
     p = _plan(384, 512, 7168, 256, 8)
     assert p.block_m == 16 and p.tok_e_x100 == 533 and p.split_k == 1
-    assert p.waves_k == 1 and p.block_n == 128         # 383 x 4 tiles
+    # 384 x 2 items of 256 columns fill one round of the gang schedule
+    assert p.waves_k == 1 and p.block_n == 256 and p.schedule == qma.SCHEDULE_GANG
     t = _plan(8, 256, 256, 64, 2)
     assert t.block_m == 16 and t.waves_k == 1          # waves side by side on columns
     assert t.block_n == 128                            # short K: 256 wide, 8 tiles -> narrower
     assert t.split_k == 1                              # K = 256: no room to split
     d = _plan(48, 7168, 2048, 576, 1)                  # EP8 down: K = 2048
     assert d.waves_k == 1 and d.block_n == 128 and d.split_k == 1
+    assert d.schedule == qma.SCHEDULE_SEMI_STATIC      # 2688 items: several rounds
     m = _plan(48, 4096, 7168, 48 * 32, 1)              # 32-row tiles: 256 columns
     assert m.block_m == 32 and m.waves_k == 1 and m.block_n == 256
     big = _plan(48, 4096, 7168, 48 * 64, 1)            # 64-row tiles: shared rows, 128 wide
@@ -180,9 +184,34 @@ def test_stream_rule():
     assert _plan(8, 256, 128, 64, 2).n_stream == 1          # grid too small to stream
 
 
+def test_gang_schedule_plan_rules():
+    # taken where the items fill 5/6 to all of one round of 3 x 256 groups
+    for E, T, gang in [(48, 576, True), (40, 480, True), (39, 468, False), (49, 588, False),
+                       (24, 288, True), (19, 228, False)]:
+        p = _plan(E, 4096, 7168, T, 1)
+        assert (p.schedule == qma.SCHEDULE_GANG) == gang, (E, p.est_tiles)
+    # never for short K, streaming, K split across waves, split-K or large-M
+    assert _plan(384, 7168, 256, 256, 8).schedule == qma.SCHEDULE_SEMI_STATIC
+    assert _plan(12, 4096, 7168, 144, 1).schedule == qma.SCHEDULE_SEMI_STATIC   # waves_k 2
+    assert _plan(3, 4096, 7168, 36, 1).schedule == qma.SCHEDULE_SEMI_STATIC     # split-K
+    assert _plan(48, 4096, 7168, 48 * 100, 1).schedule == qma.SCHEDULE_SEMI_STATIC
+    # 12 tiles dealt to 8 XCDs: four XCDs hold 2 x 56 items, more than one
+    # round of their 32 x 3 groups
+    assert _plan(12, 7168, 2048, 144, 1).schedule == qma.SCHEDULE_SEMI_STATIC
+    # masked decode (32-row tiles): 48 x 16 items
+    lay = qma.qma_layer_create(48, 4096, 7168, qma.PATH_GROUPED_MASKED)
+    try:
+        m = qma.qma_plan_grouped(lay, 64, 32)
+    finally:
+        qma.qma_layer_destroy(lay)
+    assert m.block_m == 32 and m.block_n == 256 and m.schedule == qma.SCHEDULE_GANG
+    assert qma.qma_workspace_bytes(m) == 0
+
+
 def test_dynamic_schedule_plan_rules():
     p = _plan(48, 4096, 7168, 576, 1)
-    assert p.schedule == qma.SCHEDULE_SEMI_STATIC and qma.qma_workspace_bytes(p) == 0
+    p.schedule = qma.SCHEDULE_SEMI_STATIC
+    assert qma.qma_workspace_bytes(p) == 0
     p.schedule = qma.SCHEDULE_DYNAMIC
     assert qma.qma_workspace_bytes(p) == 256           # the work counter
     q = _plan(1, 4096, 7168, 12, 1)                    # split-K plan
@@ -362,6 +391,14 @@ def test_planner_invariants_over_shapes():
             assert shared or tm * ntw <= 4, shape
             if p.n_stream > 1:                               # streaming: short K only
                 assert K // 128 < 8 and p.block_m == 16 and p.split_k == 1, shape
+            if p.schedule == qma.SCHEDULE_GANG:
+                # a shared-row instance, one K partition, one round of groups
+                assert shared and p.n_stream == 1 and p.split_k == 1, shape
+                assert 640 <= p.est_tiles <= 768 and K // 128 >= 8, shape
+                tiles_m = p.est_tiles // (N // p.block_n)
+                assert -(-tiles_m // 8) * (N // p.block_n) <= 96, shape
+            else:
+                assert p.schedule == qma.SCHEDULE_SEMI_STATIC, shape
         if p.split_k > 1:
             # split-K only when the grid underfills the CUs, and never below
             # 14 128-wide K chunks per split (four for large-M)

@@ -6,7 +6,7 @@ an edited plan can launch must run without scratch: a spilled VGPR turns
 into a private-memory round trip inside the K loop. The shared-row small-M
 instances must also fit the workgroups per compute unit they are built for
 (four: at most 128 VGPRs and a quarter of the LDS; three for the 32-row,
-4-tile instance).
+4-tile instance), and the gang instances one workgroup of three groups.
 """
 import os
 import re
@@ -50,7 +50,8 @@ def resources(tmp_path_factory):
 
 def test_every_kernel_reports(resources):
     names = " ".join(resources)
-    for k in ("gemm_small_m_xs_kernel", "gemm_small_m_xs_dyn_kernel", "gemm_small_m_kernel",
+    for k in ("gemm_small_m_xs_kernel", "gemm_small_m_xs_dyn_kernel",
+              "gemm_small_m_xs_gang_kernel", "gemm_small_m_kernel",
               "gemm_small_m_stream_kernel", "gemm_large_m_kernel", "gemm_large_m_pc_kernel",
               "splitk_reduce_kernel", "moe_align_kernel"):
         assert k in names, k
@@ -72,3 +73,14 @@ def test_shared_row_instances_fit_their_occupancy(resources):
         per_cu = 3 if "ILi2ELi4E" in n else 4
         assert r["VGPRs"] <= 512 // per_cu // 8 * 8, (n, r["VGPRs"])
         assert r["LDS Size"] <= 160 * 1024 // per_cu, (n, r["LDS Size"])
+
+
+def test_gang_instances_fit_one_workgroup_per_cu(resources):
+    # three four-wave groups per workgroup: three waves per SIMD, so at most
+    # 512 // 3 VGPRs rounded down to the allocation granule, and the groups'
+    # LDS within one CU's 160 KiB
+    gang = {n: r for n, r in resources.items() if "gemm_small_m_xs_gang_kernel" in n}
+    assert len(gang) == 5, sorted(gang)
+    for n, r in gang.items():
+        assert r["VGPRs"] <= 512 // 3 // 8 * 8, (n, r["VGPRs"])
+        assert r["LDS Size"] <= 160 * 1024, (n, r["LDS Size"])

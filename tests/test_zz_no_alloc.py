@@ -24,6 +24,8 @@ def _call(rng, E, T, topk, K, N, force_bm=0, override=None):
     ids = rng.integers(0, E, (T, topk)).astype(np.int32)
     W = ExpertWeights(w, s)
     plan = qma.qma_plan_indexed(W.layer, T, topk, force_bm)
+    if override:
+        plan.schedule = qma.SCHEDULE_SEMI_STATIC   # unless the override names one
     for k, v in (override or {}).items():
         setattr(plan, k, v)
     B = plan.block_m
