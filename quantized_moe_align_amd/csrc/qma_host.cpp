@@ -88,9 +88,7 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     while (ntw > 1 && L.N % (64 * ntw) != 0) ntw /= 2;
     // Wave-aware width: the narrower width when the wide one leaves CUs
     // without a workgroup, down to 128 columns; an underfilled grid is then
-    // left to split-K. (64 columns would leave the shared-row kernel: on an
-    // EP128 share, 3 experts, that ran gate_up in 60.5 us at split 2 against
-    // 30.6 us at 128 columns and split 4, and down in 34.5 against 20.3 us.)
+    // left to split-K, or below (64 columns) when K is too short to split.
     if (ntw > 2 && (int64_t)tiles_m * (L.N / (64 * ntw)) < qma::kNumCUs &&
         L.N % (64 * (ntw / 2)) == 0)
       ntw /= 2;
@@ -136,15 +134,28 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->est_tiles = tiles;
   // Split-K gate: only when the grid underfills the CUs. It then aims at
   // 1.5 workgroups per CU, never below kSplitChunks 128-wide K chunks per
-  // split. (EP128 gate_up, 96 tiles, K = 56 chunks: split 3/4/6/8 ran
-  // 31.4/30.6/32.1/34.8 us; down, 168 tiles, K = 16 chunks: unsplit 20.3 us,
-  // split 2-3 21.2-23.6 us.)
+  // split. (EP128 gate_up, 96 tiles, K = 56 chunks: split 2/3/4/6/8 ran
+  // 29.9/25.6/23.0/22.5/22.0 us with the tiles folded over all XCDs, 1: 45 us;
+  // down, 168 tiles, K = 16 chunks: split 2 no faster than unsplit.)
   int32_t split = 1;
   if (tiles < qma::kNumCUs) {
     const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / qma::kSplitChunks));
     split = std::min<int32_t>(
         {ceil_div(3 * qma::kNumCUs / 2, std::max(tiles, 1)), max_split, 8});
     split = std::max<int32_t>(split, 1);
+  }
+  // An underfilled grid that K is too short to split (an EP128 down share:
+  // 3 tiles x 56 blocks of 128 columns, 16 chunks) takes 64-column blocks,
+  // one column tile per wave and the waves on K, for twice the workgroups:
+  // 16.7 -> 13.2 us. (With long K, split-K stays ahead: EP128 gate_up at
+  // 64 columns and split 2 ran 21.6 us against 23.0 at 128 and split 4.)
+  if (split == 1 && tiles < qma::kNumCUs && tm == 1 && wk == 1 && L.N % 64 == 0 &&
+      L.k_chunks >= qma::kStreamChunks) {
+    wk = 4;
+    ntw = 1;
+    p->waves_k = wk;
+    p->block_n = 64;
+    p->est_tiles = (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / 64), 1 << 30);
   }
   p->split_k = split;
   // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
@@ -177,12 +188,14 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     const int64_t slots = (int64_t)qma::kGangGroups * qma::kNumCUs;
     for (const int cand : {ntw, 4, 2}) {
       if (!qma::small_m_shared_rows(tm, cand, 1) || L.N % (64 * cand) != 0) continue;
-      // token tiles are dealt to the 8 XCDs in turn, all column blocks of a
-      // tile on one XCD: the fullest XCD must fit one round too (an EP32
-      // down share, 12 tiles x 56 blocks, has 112 items on four XCDs and ran
-      // 40.9 us this way against 28.6 us semi-static)
-      const int64_t items = (int64_t)tiles_m * (L.N / (64 * cand));
-      const int64_t per_xcd = ceil_div(tiles_m, 8) * (int64_t)(L.N / (64 * cand));
+      // token tiles (folded into column-block groups where few) are dealt
+      // to the 8 XCDs in turn: the fullest XCD must fit one round too (an
+      // EP32 down share without folding, 12 tiles x 56 blocks, had 112 items
+      // on four XCDs and ran 40.9 us this way against 28.6 us semi-static)
+      const int64_t nbc = L.N / (64 * cand);
+      const int64_t items = (int64_t)tiles_m * nbc;
+      const int f = qma::xcd_fold(tiles_m, nbc);
+      const int64_t per_xcd = ceil_div((int64_t)tiles_m * f, 8) * (nbc / f);
       if (per_xcd > slots / 8 || 6 * items < qma::kGangMinFill * slots) continue;
       p->block_n = 64 * cand;
       p->est_tiles = (int32_t)items;

@@ -45,6 +45,25 @@ constexpr int kStreamTargetChunks = 14;
 // streaming
 constexpr int kSplitChunks = 14;
 constexpr int kLdsPerCU = 160 * 1024;
+// Small-M launches deal token tiles to the 8 XCDs in turn, all column blocks
+// of a tile on one XCD, so that its rows stay in that XCD's L2. With few
+// tiles that leaves XCDs idle or uneven (an EP128 share: 3 tiles on 3 of
+// the 8 XCDs). The fold splits each tile's column blocks into f groups
+// dealt as separate tiles (each XCD then reads the rows of the tiles it
+// holds): the smallest f in {1, 2, 4, 8} dividing nblocks whose t * f
+// virtual tiles fill the 8 XCDs to within 10 % of even.
+inline int xcd_fold(int64_t tiles, int64_t nblocks) {
+  if (tiles <= 0) return 1;
+  for (int f = 1; f <= 8; f *= 2) {
+    if (nblocks % f != 0) break;
+    const int64_t v = tiles * f;
+    if ((v + 7) / 8 * 8 * 10 <= v * 11) return f;
+  }
+  int f = 8;
+  while (f > 1 && nblocks % f != 0) f /= 2;
+  return f;
+}
+
 // Gang schedule: four-wave groups per workgroup, one workgroup per CU. The
 // planner takes it for a shared-row GEMM whose planned items fill between
 // kGangMinFill sixths and all of one round of kGangGroups * kNumCUs slots.

@@ -317,6 +317,7 @@ struct GemmParams {
   int32_t nstream, nbtot;  // streaming small-M: N blocks per workgroup, N blocks in all
   int32_t* work;            // dynamic schedule: work counter (workspace)
   int32_t wg_log2;          // packed layout: log2 of the tiles per block group
+  int32_t fold;             // column-block groups per tile dealt to the XCDs (divides nblocks)
 };
 
 // Place of 16-column tile t0 + j, K chunk c inside one expert's packed
@@ -503,20 +504,24 @@ __device__ __forceinline__ void wait_lgkm(u32x4& v) {
   asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(v) : "n"(N));
 }
 
-// Decode the XCD-aware workgroup order. Workgroup i runs on XCD i % 8, and
-// XCD x takes token tiles x, x+8, ... with all of their (column block,
-// split) pieces. A tile's activations then stay in one XCD's L2, and empty
+// Decode the XCD-aware workgroup order. Workgroup i runs on XCD i % 8. The
+// column blocks of a token tile form p.fold groups, each a virtual tile
+// (tile * fold + group), and XCD x takes virtual tiles x, x+8, ... with all
+// of their (column block, split) pieces. A tile's activations then stay in
+// the L2 of the XCDs that hold its groups (one without folding), and empty
 // tiles spread evenly over the XCDs.
 __device__ __forceinline__ bool decode_bid(const GemmParams& p, int bid, int& tile, int& nb,
                                            int& sp) {
   const int xcd = bid & 7;
   const int idx = bid >> 3;
-  const int per_tile = p.nblocks * p.split;
-  const int j = idx / per_tile;
-  const int rem = idx - j * per_tile;
-  tile = xcd + 8 * j;
-  nb = rem / p.split;
-  sp = rem - nb * p.split;
+  const int nbf = p.nblocks / p.fold;
+  const int per_vt = nbf * p.split;
+  const int j = idx / per_vt;
+  const int rem = idx - j * per_vt;
+  const int vt = xcd + 8 * j;
+  tile = vt / p.fold;
+  nb = (vt - tile * p.fold) * nbf + rem / p.split;
+  sp = rem % p.split;
   return tile < p.num_tiles;
 }
 
@@ -2213,6 +2218,12 @@ static int launch_xs_gang(const GemmParams& gp, int64_t items, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
+// Token tiles the plan expects (its estimate, est_tiles / column blocks).
+static int64_t plan_tiles_m(const qma_plan_t& pl) {
+  const int64_t nb = pl.block_n > 0 ? pl.n / pl.block_n : 0;
+  return nb > 0 ? pl.est_tiles / nb : 0;
+}
+
 int launch_gemm(const GemmArgs& g, void* stream) {
   const Layer& L = *g.layer;
   const qma_plan_t& pl = *g.plan;
@@ -2247,6 +2258,7 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   gp.KC = (int32_t)L.k_chunks;
   gp.BM = pl.block_m;
   gp.wg_log2 = L.wg_log2;
+  gp.fold = 1;
   const int64_t tiles_pad = (g.num_tiles + 7) / 8 * 8;
   const int64_t grid = tiles_pad * gp.nblocks * gp.split;
   if (grid <= 0) return 0;
@@ -2306,7 +2318,9 @@ int launch_gemm(const GemmArgs& g, void* stream) {
     gp.nstream = pl.n_stream;
     gp.nbtot = gp.nblocks;
     gp.nblocks = (gp.nbtot + gp.nstream - 1) / gp.nstream;
-    const dim3 sg((unsigned)(tiles_pad * gp.nblocks * gp.split));
+    gp.fold = xcd_fold(plan_tiles_m(pl), gp.nblocks);
+    const int64_t vt_pad = ((int64_t)g.num_tiles * gp.fold + 7) / 8 * 8;
+    const dim3 sg((unsigned)(vt_pad * (gp.nblocks / gp.fold) * gp.split));
     if (pl.schedule == QMA_SCHEDULE_GANG) {
       if (!xs) return (int)hipErrorInvalidConfiguration;
       if (tm == 1 && ntw == 4)
@@ -2339,8 +2353,11 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   } else {
     if (!small_m_wave_rows(tm, ntw, wk) || ntw * 16 * (4 / wk) != pl.block_n)
       return (int)hipErrorInvalidConfiguration;
+    gp.fold = xcd_fold(plan_tiles_m(pl), gp.nblocks);
+    const int64_t vt_pad = ((int64_t)g.num_tiles * gp.fold + 7) / 8 * 8;
+    const unsigned wgrid = (unsigned)(vt_pad * (gp.nblocks / gp.fold) * gp.split);
 #define QMA_SMALL_M_CASE(TM_, NTW_) \
-  if (tm == TM_ && ntw == NTW_) err = launch_small_m_wk<TM_, NTW_>(gp, (unsigned)grid, st, wk, depth);
+  if (tm == TM_ && ntw == NTW_) err = launch_small_m_wk<TM_, NTW_>(gp, wgrid, st, wk, depth);
     QMA_SMALL_M_CASE(1, 1)
     QMA_SMALL_M_CASE(1, 2)
     QMA_SMALL_M_CASE(1, 4)

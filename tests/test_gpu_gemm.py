@@ -771,6 +771,45 @@ def test_gang_schedule_grouped(gpu):
         assert np.all(got_m[row_e < 0] == SENT)
 
 
+# Few token tiles are folded into column-block groups dealt to the XCDs
+# separately (the fold follows the plan's tile estimate, est_tiles / column
+# blocks). Folding moves work between workgroups only: every fold gives the
+# unfolded output bit for bit, on every kernel family that deals tiles that
+# way, and the oracle with integer-exact inputs.
+FOLD_PLANS = [
+    {"block_n": 128, "waves_k": 1, "split_k": 1, "n_stream": 1},
+    {"block_n": 128, "waves_k": 1, "split_k": 1, "n_stream": 1, "schedule": qma.SCHEDULE_GANG},
+    {"block_n": 256, "waves_k": 1, "split_k": 2, "n_stream": 1},
+    {"block_n": 64, "waves_k": 4, "split_k": 1, "n_stream": 1},
+    {"block_n": 128, "waves_k": 2, "split_k": 1, "n_stream": 1},
+    {"block_n": 128, "waves_k": 1, "split_k": 1, "n_stream": 2},
+]
+
+
+@pytest.mark.parametrize("plan_i", range(len(FOLD_PLANS)))
+def test_xcd_fold_bitwise(gpu, plan_i):
+    E, T, topk, N = 5, 60, 2, 2048
+    ov = FOLD_PLANS[plan_i]
+    K = 256 if ov["n_stream"] > 1 else 1024
+    rng = np.random.default_rng(360 + plan_i)
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    nb = N // ov["block_n"]
+    outs = []
+    for tiles_est in (1 << 12, 3, 12, 1):        # fold 1, then 8, 2 and 8
+        got, plan = indexed(a, topk, ids, w, s, force_bm=16,
+                            override=dict(ov, kernel=qma.KERNEL_SMALL_M, block_m=16,
+                                          est_tiles=tiles_est * nb))
+        outs.append(got)
+    for got in outs[1:]:
+        assert np.array_equal(got, outs[0])
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(outs[0][valid], rne(ref[valid]))
+    assert np.all(outs[0][~valid] == SENT)
+
+
 def test_gang_schedule_with_nothing_routed(gpu):
     E, T, topk, K, N = 6, 50, 2, 1024, 512
     rng = np.random.default_rng(330)

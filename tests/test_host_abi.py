@@ -144,11 +144,12 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     assert p.block_n == 128 and p.est_tiles == 32 and p.split_k == 4 and p.waves_k == 1
     assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
     # EP128 share (3 experts): gate_up 96 tiles -> split 4; down (K = 16
-    # chunks) has no room for two runs of 14 -> unsplit, still 128 wide
+    # chunks) has no room for two runs of 14 -> unsplit, 64 columns with
+    # the waves on K for twice the workgroups
     g = _plan(3, 4096, 7168, 35, 1)
     assert g.block_n == 128 and g.est_tiles == 96 and g.split_k == 4
     d = _plan(3, 7168, 2048, 35, 1)
-    assert d.block_n == 128 and d.est_tiles == 168 and d.split_k == 1
+    assert d.block_n == 64 and d.waves_k == 4 and d.est_tiles == 336 and d.split_k == 1
     # 8 experts: 256 tiles at 128 columns -> no split
     assert _plan(8, 4096, 7168, 96, 1).split_k == 1
     # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> no split; between one
@@ -195,9 +196,8 @@ def test_gang_schedule_plan_rules():
     assert _plan(12, 4096, 7168, 144, 1).schedule == qma.SCHEDULE_SEMI_STATIC   # waves_k 2
     assert _plan(3, 4096, 7168, 36, 1).schedule == qma.SCHEDULE_SEMI_STATIC     # split-K
     assert _plan(48, 4096, 7168, 48 * 100, 1).schedule == qma.SCHEDULE_SEMI_STATIC
-    # 12 tiles dealt to 8 XCDs: four XCDs hold 2 x 56 items, more than one
-    # round of their 32 x 3 groups
-    assert _plan(12, 7168, 2048, 144, 1).schedule == qma.SCHEDULE_SEMI_STATIC
+    # 12 tiles folded into 24 column-block groups: 3 x 28 items per XCD
+    assert _plan(12, 7168, 2048, 144, 1).schedule == qma.SCHEDULE_GANG
     # masked decode (32-row tiles): 48 x 16 items
     lay = qma.qma_layer_create(48, 4096, 7168, qma.PATH_GROUPED_MASKED)
     try:
@@ -364,6 +364,32 @@ def test_missing_library_fails_loudly():
     assert "raised" in r.stdout and "not built" in r.stdout, r.stdout + r.stderr
 
 
+def xcd_fold(tiles, nblocks):
+    """The launch's fold of few token tiles into column-block groups dealt
+    to the 8 XCDs: the smallest f in (1, 2, 4, 8) dividing nblocks that fills
+    the XCDs to within 10 % of even (written out here from that rule)."""
+    if tiles <= 0:
+        return 1
+    for f in (1, 2, 4, 8):
+        if nblocks % f:
+            break
+        v = tiles * f
+        if -(-v // 8) * 8 * 10 <= v * 11:
+            return f
+    f = 8
+    while f > 1 and nblocks % f:
+        f //= 2
+    return f
+
+
+def test_xcd_fold_rule():
+    assert xcd_fold(3, 32) == 8 and xcd_fold(3, 56) == 8      # EP128: 24 groups
+    assert xcd_fold(12, 56) == 2 and xcd_fold(24, 28) == 1    # EP32, EP16
+    assert xcd_fold(48, 16) == 1 and xcd_fold(384, 2) == 1    # EP8, TP8
+    assert xcd_fold(3, 28) == 4                               # 4 divides 28, 8 does not
+    assert xcd_fold(5, 7) == 1                                # nothing divides 7
+
+
 def test_planner_invariants_over_shapes():
     # every plan the planner returns names an existing kernel instance and
     # follows the documented rules, over a grid of layer and batch shapes
@@ -395,8 +421,10 @@ def test_planner_invariants_over_shapes():
                 # a shared-row instance, one K partition, one round of groups
                 assert shared and p.n_stream == 1 and p.split_k == 1, shape
                 assert 640 <= p.est_tiles <= 768 and K // 128 >= 8, shape
-                tiles_m = p.est_tiles // (N // p.block_n)
-                assert -(-tiles_m // 8) * (N // p.block_n) <= 96, shape
+                nb = N // p.block_n
+                tiles_m = p.est_tiles // nb
+                f = xcd_fold(tiles_m, nb)
+                assert -(-tiles_m * f // 8) * (nb // f) <= 96, shape
             else:
                 assert p.schedule == qma.SCHEDULE_SEMI_STATIC, shape
         if p.split_k > 1:
