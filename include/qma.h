@@ -139,7 +139,8 @@ typedef struct qma_plan {
   int32_t k;             /* K of the layer */
   int32_t rows;          /* rows planned for: T*topk, M, or E*budget */
   int32_t tok_e_x100;    /* routed rows per expert x 100, host estimate */
-  int32_t est_tiles;     /* M x N tiles expected without split-K */
+  int32_t est_tiles;     /* M x N tiles expected without split-K; the launch also
+                            spreads few token tiles over the XCDs from it */
   int32_t profile;       /* qma_profile */
   int32_t waves_k;       /* K partitions inside one workgroup */
   int32_t expected_m;    /* masked layers: the expected_m planned for, else 0 */
