@@ -152,7 +152,7 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   if (split == 1 && tiles < qma::kNumCUs && tm == 1 && wk == 1 && L.N % 64 == 0 &&
       L.k_chunks >= qma::kStreamChunks) {
     wk = 4;
-    ntw = 1;
+    ntw = 4;                 // one wave column of four 16-column tiles
     p->waves_k = wk;
     p->block_n = 64;
     p->est_tiles = (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / 64), 1 << 30);
