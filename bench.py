@@ -2,9 +2,11 @@
 """Benchmark of the W4A16 MoE expert GEMM pair on one MI355X.
 
 One step is one pass of the whole hot path over one batch. On the indexed
-path that is moe_align, gate_up, silu_and_mul and down; on the grouped
-paths it is gate_up, silu_and_mul and down. Inputs are resident in HBM
-before timing starts.
+path that is moe_align, gate_up, the activation silu(gate) * up, and down;
+on the grouped paths it is gate_up, the activation and down. By default the
+activation runs in gate_up's epilogue (a gate_up layer made with the fused
+flag); --activation separate runs it as its own kernel (silu_and_mul)
+between the GEMMs. Inputs are resident in HBM before timing starts.
 
 The headline workload (--workload, default the EP8 decode share) gives
 `value`: W warm-up steps run untimed (continued until the step has run back
@@ -76,7 +78,7 @@ DESCRIPTIONS = {
 }
 
 
-def algorithmic_work(wl):
+def algorithmic_work(wl, fused=False):
     """Bytes each GEMM must move and flops it must do: packed weights and
     scales of experts that have rows (0.5625 B per weight), distinct
     activation rows read once, output rows written once; 2*rows*N*K flops
@@ -99,7 +101,8 @@ def algorithmic_work(wl):
     ne = int((counts > 0).sum())
     w13 = ne * 2 * I * K * 9 // 16
     w2 = ne * K * I * 9 // 16
-    gu_bytes = w13 + a_rows * K * 2 + rows * 2 * I * 2
+    # gate_up writes h [rows, I] with the activation fused, else [rows, 2I]
+    gu_bytes = w13 + a_rows * K * 2 + rows * (1 if fused else 2) * I * 2
     dn_bytes = w2 + rows * I * 2 + rows * K * 2
     return {"rows": rows, "experts_with_rows": ne,
             "gate_up_bytes": gu_bytes, "down_bytes": dn_bytes,
@@ -361,21 +364,23 @@ class WeightCache:
         wl.arrays.update(self.host[key])
         return key
 
-    def packed(self, key, path):
+    def packed(self, key, path, fused=False):
         from quantized_moe_align_amd import qma
         from quantized_moe_align_amd.moe import ExpertWeights
-        if key not in self.dev:
+        dkey = (key, fused)
+        if dkey not in self.dev:
             h = self.host[key]
-            self.dev[key] = {qma.PATH_INDEXED: (ExpertWeights(h["w13"], h["s13"]),
-                                                ExpertWeights(h["w2"], h["s2"]))}
-        d = self.dev[key]
+            flags = qma.LAYER_FUSE_SILU_MUL if fused else 0
+            self.dev[dkey] = {qma.PATH_INDEXED: (ExpertWeights(h["w13"], h["s13"], flags=flags),
+                                                 ExpertWeights(h["w2"], h["s2"]))}
+        d = self.dev[dkey]
         if path not in d:
             base13, base2 = d[qma.PATH_INDEXED]
             d[path] = (base13.with_path(path), base2.with_path(path))
         return d[path]
 
 
-def build_runner(name, seed, cache, schedule, overrides):
+def build_runner(name, seed, cache, schedule, overrides, fused=True):
     """Inputs on the device and the step's stages for one workload."""
     import torch
     from quantized_moe_align_amd import inputs, qma
@@ -383,18 +388,20 @@ def build_runner(name, seed, cache, schedule, overrides):
 
     wl = inputs.make(name, seed=seed, weights=False)
     key = cache.attach(wl, seed)
-    work = algorithmic_work(wl)
+    work = algorithmic_work(wl, fused)
     if wl.kind == "indexed":
-        w13, w2 = cache.packed(key, qma.PATH_INDEXED)
+        w13, w2 = cache.packed(key, qma.PATH_INDEXED, fused)
         moe = IndexedMoE(w13, w2, wl.T, wl.topk)
         a = to_device(wl["a"])
         ids = to_device(wl["topk_ids"])
         stages = [("moe_align", lambda: moe.align(ids)), ("gate_up", lambda: moe.gate_up(a)),
                   ("silu_and_mul", moe.act), ("down", lambda: moe.down())]
+        if fused:
+            del stages[2]
     else:
         path = (qma.PATH_GROUPED_CONTIGUOUS if wl.kind == "contiguous"
                 else qma.PATH_GROUPED_MASKED)
-        w13, w2 = cache.packed(key, path)
+        w13, w2 = cache.packed(key, path, fused)
         if wl.kind == "contiguous":
             index = to_device(wl["m_indices"])
             moe = GroupedMoE(w13, w2, wl["m_indices"].size)
@@ -404,6 +411,8 @@ def build_runner(name, seed, cache, schedule, overrides):
         a = to_device(wl["a"])
         stages = [("gate_up", lambda: moe.gate_up(a, index)), ("silu_and_mul", moe.act),
                   ("down", lambda: moe.down(index))]
+        if fused:
+            del stages[1]
     applied = (False, False)
     if schedule != "planner":
         applied = moe.set_schedule({"semi_static": qma.SCHEDULE_SEMI_STATIC,
@@ -541,6 +550,9 @@ def main():
                     help="seconds of oracle CPU work for cpu_baseline (0 = skip the CPU legs)")
     ap.add_argument("--cpu-fp32-experts", type=int, default=4,
                     help="experts in the fp32 NumPy legs of cpu_baseline")
+    ap.add_argument("--activation", default="fused", choices=("fused", "separate"),
+                    help="silu(gate) * up in gate_up's epilogue (fused, the default) or as its "
+                         "own kernel between the GEMMs (separate)")
     ap.add_argument("--schedule", default="planner",
                     choices=("planner", "semi_static", "dynamic", "gang"),
                     help="how small-M GEMMs hand out (tile, column block) work: the "
@@ -596,7 +608,8 @@ def main():
              if args.flush and configs else None)
 
     # headline workload
-    r = build_runner(args.workload, args.seed, cache, args.schedule, overrides)
+    fused = args.activation == "fused"
+    r = build_runner(args.workload, args.seed, cache, args.schedule, overrides, fused)
     m = measure(r, args.steps, args.warmup, args.settle_ms, args.idle_gap_ms)
     work, moe, ev = r["work"], r["moe"], m["ev"]
     ms_per_step = m["ms_per_step"]
@@ -636,6 +649,7 @@ def main():
                    "rows": work["rows"], "weights": "uint4 group-32 bf16 scales, zero point 8",
                    "parallelism": "one EP/TP rank's share on one GPU",
                    "schedule": sched,
+                   "activation": "fused into gate_up" if fused else "separate kernel",
                    **({"plan_overrides": overrides} if any(overrides.values()) else {}),
                    **({"idle_gap_ms": args.idle_gap_ms} if args.idle_gap_ms > 0 else {})},
         "us_per_layer_gate_up_down": round(us["gate_up"] + us["down"], 2),
@@ -656,7 +670,7 @@ def main():
     if configs:
         cfg_out = {}
         for name in configs:
-            rc = build_runner(name, args.seed, cache, "planner", {})
+            rc = build_runner(name, args.seed, cache, "planner", {}, fused)
             mc = measure(rc, args.steps, args.warmup, min(args.settle_ms, 150.0), flush=flush)
             rep = pair_report(name, rc["work"], mc["ev"], read_traffic(name))
             rep["ms_per_step"] = round(mc["ms_per_step"], 4)

@@ -194,6 +194,29 @@ typedef enum {
  * caller owns *out and frees it with qma_layer_destroy. */
 qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
                             int32_t K, qma_path path, qma_layer_t** out);
+
+/* Layer flags for qma_layer_create_ex. */
+typedef enum {
+  /* A gate_up layer with the gated activation fused into its GEMMs
+   * ([announce] measurement section: an activation, silu(gate) * up, sits
+   * between gate_up and down). The checkpoint has N = 2I rows: gate rows
+   * [0, I), then up rows [I, 2I). The GEMMs of such a layer write
+   * h = silu(gate) * up, [rows, I] bf16 with row stride I, instead of the
+   * [rows, 2I] gate_up output; gate and up are each rounded to bf16 first,
+   * as the unfused GEMM stores them, so h equals qma_silu_and_mul on the
+   * unfused output bit for bit. The packed layout pairs gate tile q with up
+   * tile q (qma_prepack writes it). Needs N % 64 == 0; a plan must give each
+   * wave an even number of 16-column tiles (every planner plan does) and
+   * must not name QMA_KERNEL_LARGE_M_PC -> QMA_ERR_INVALID_ARG. Split-K
+   * partials stay in the packed column order and the reduction applies the
+   * activation. */
+  QMA_LAYER_FUSE_SILU_MUL = 1
+} qma_layer_flag;
+
+/* qma_layer_create with flags (qma_layer_flag bits; 0 is qma_layer_create).
+ * Unknown bits -> QMA_ERR_INVALID_ARG. */
+qma_status qma_layer_create_ex(const qma_quant_desc* q, int32_t E, int32_t N, int32_t K,
+                               qma_path path, uint32_t flags, qma_layer_t** out);
 void qma_layer_destroy(qma_layer_t* layer);
 /* Reads back the shape, path and inferred profile. Null outputs are
  * skipped. */

@@ -317,7 +317,14 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
         !qma::small_m_supported(plan->block_m / 16, plan->block_n / (16 * wn), wk))
       return fail(QMA_ERR_INVALID_ARG, "no small-M kernel for a %d x %d block with waves_k %d",
                   plan->block_m, plan->block_n, wk);
+    // fused activation: each wave must hold gate and up tiles in pairs
+    if (L.act && (plan->block_n / (16 * wn)) % 2 != 0)
+      return fail(QMA_ERR_INVALID_ARG,
+                  "a fused gate_up layer needs an even tile count per wave (block_n %d, waves_k %d)",
+                  plan->block_n, wk);
   }
+  if (L.act && plan->kernel == QMA_KERNEL_LARGE_M_PC)
+    return fail(QMA_ERR_INVALID_ARG, "the producer/consumer kernel has no fused activation");
   return ok();
 }
 
@@ -361,6 +368,11 @@ const char* qma_version(void) { return "qma 0.1 gfx950"; }
 
 qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
                             int32_t K, qma_path path, qma_layer_t** out) {
+  return qma_layer_create_ex(q, E, N, K, path, 0, out);
+}
+
+qma_status qma_layer_create_ex(const qma_quant_desc* q, int32_t E, int32_t N, int32_t K,
+                               qma_path path, uint32_t flags, qma_layer_t** out) {
   if (!q || !out) return fail(QMA_ERR_INVALID_ARG, "null descriptor or out");
   *out = nullptr;
   if (q->weight_bits != 4)
@@ -382,6 +394,11 @@ qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
     return fail(QMA_ERR_INVALID_ARG, "bad shape E=%d N=%d K=%d", E, N, K);
   if (N % 16 != 0) return fail(QMA_ERR_INVALID_ARG, "N=%d is not a multiple of 16", N);
   if (K % 128 != 0) return fail(QMA_ERR_INVALID_ARG, "K=%d is not a multiple of 128", K);
+  if (flags & ~(uint32_t)QMA_LAYER_FUSE_SILU_MUL)
+    return fail(QMA_ERR_INVALID_ARG, "unknown layer flags 0x%x", flags);
+  const bool fuse = flags & QMA_LAYER_FUSE_SILU_MUL;
+  if (fuse && N % 64 != 0)
+    return fail(QMA_ERR_INVALID_ARG, "a fused gate_up layer needs N %% 64 == 0 (N=%d)", N);
   auto* l = new (std::nothrow) qma_layer_t;
   if (!l) return fail(QMA_ERR_INVALID_ARG, "out of host memory");
   Layer& L = l->L;
@@ -389,6 +406,7 @@ qma_status qma_layer_create(const qma_quant_desc* q, int32_t E, int32_t N,
   L.N = N;
   L.K = K;
   L.path = path;
+  L.act = fuse ? 1 : 0;
   L.profile = infer_profile(E, N, K);
   L.n_tiles = N / qma::kTileN;
   L.k_chunks = K / qma::kChunkK;

@@ -80,6 +80,7 @@ struct Layer {
   int32_t path;
   int32_t profile;
   int32_t wg_log2;     // log2 of the tiles per block group (packed layout)
+  int32_t act;         // 1: gate_up layer with silu(gate) * up fused (packed tiles interleaved)
   int64_t n_tiles;     // N / 16
   int64_t k_chunks;    // K / 128
   size_t w_bytes;      // weight region

@@ -229,16 +229,23 @@ __device__ __forceinline__ void block_place(int64_t b, int64_t n_tiles, int64_t 
   e = rest / groups;
 }
 
+// Packed tile nt -> checkpoint tile. A gate_up layer with the activation
+// fused keeps gate tile q and up tile q side by side (packed 2q, 2q + 1).
+__device__ __forceinline__ int64_t source_tile(int64_t nt, int64_t n_tiles, int32_t act) {
+  if (!act) return nt;
+  return (nt & 1) ? n_tiles / 2 + (nt >> 1) : (nt >> 1);
+}
+
 __global__ void prepack_weights_kernel(const uint32_t* __restrict__ qw, uint32_t* __restrict__ out,
                                        int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
-                                       int32_t wg_log2, int64_t total) {
+                                       int32_t wg_log2, int32_t act, int64_t total) {
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
     const int j = (int)(o & 3);
     const int l = (int)((o >> 2) & 63);
     int64_t e, nt, kc;
     block_place(o >> 8, n_tiles, k_chunks, wg_log2, e, nt, kc);
-    const int64_t n = nt * 16 + (l & 15);
+    const int64_t n = source_tile(nt, n_tiles, act) * 16 + (l & 15);
     const int64_t k0 = kc * 128 + j * 32 + (l >> 4) * 8;
     out[o] = interleave_nibbles(qw[(e * N + n) * (K / 8) + k0 / 8]);
   }
@@ -246,14 +253,14 @@ __global__ void prepack_weights_kernel(const uint32_t* __restrict__ qw, uint32_t
 
 __global__ void prepack_scales_kernel(const uint16_t* __restrict__ sc, uint16_t* __restrict__ out,
                                       int32_t N, int32_t K, int64_t n_tiles, int64_t k_chunks,
-                                      int32_t wg_log2, int64_t total) {
+                                      int32_t wg_log2, int32_t act, int64_t total) {
   for (int64_t o = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; o < total;
        o += (int64_t)gridDim.x * blockDim.x) {
     const int g = (int)(o & 3);
     const int row = (int)((o >> 2) & 15);
     int64_t e, nt, kc;
     block_place(o >> 6, n_tiles, k_chunks, wg_log2, e, nt, kc);
-    const int64_t n = nt * 16 + row;
+    const int64_t n = source_tile(nt, n_tiles, act) * 16 + row;
     out[o] = sc[(e * N + n) * (K / 32) + kc * 4 + g];
   }
 }
@@ -265,10 +272,10 @@ int launch_prepack(const Layer& L, const int32_t* qweight, const uint16_t* scale
   auto blocks = [](int64_t n) { return (unsigned)std::min<int64_t>((n + 255) / 256, 65536); };
   hipLaunchKernelGGL(prepack_weights_kernel, dim3(blocks(words)), dim3(256), 0,
                      (hipStream_t)stream, (const uint32_t*)qweight, (uint32_t*)packed, L.N, L.K,
-                     L.n_tiles, L.k_chunks, L.wg_log2, words);
+                     L.n_tiles, L.k_chunks, L.wg_log2, L.act, words);
   hipLaunchKernelGGL(prepack_scales_kernel, dim3(blocks(svals)), dim3(256), 0,
                      (hipStream_t)stream, scales, (uint16_t*)((char*)packed + L.w_bytes), L.N,
-                     L.K, L.n_tiles, L.k_chunks, L.wg_log2, svals);
+                     L.K, L.n_tiles, L.k_chunks, L.wg_log2, L.act, svals);
   return (int)hipGetLastError();
 }
 
@@ -298,6 +305,31 @@ int launch_prepack(const Layer& L, const int32_t* qweight, const uint16_t* scale
 // rows the tile does not use, so those rows are never read. The WK partial
 // sums meet in LDS at the end.
 // ---------------------------------------------------------------------------
+// silu(g) * u in fp32 (the activation of the gated MLP between gate_up and
+// down: [announce] measurement section).
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  // silu(g) = g * sigmoid(g), without a branch. With h = e^(-|g|/2) (never
+  // overflows) and e^(-|g|) = h h: sigmoid(g) = 1 / (1 + h h) for g >= 0 and
+  // h h / (1 + h h) for g < 0, so silu(g) = ((g a) a) / (1 + h h) with a = 1
+  // or h. Multiplying by a twice keeps g e^g a normal number wherever it is
+  // one (e^g alone underflows below -87.3). The divisor lies in [1, 2],
+  // where the hardware reciprocal (1 ulp) replaces the correctly rounded
+  // division's scaling steps; the fp32 result stays far inside one bf16 ulp
+  // of the exact value.
+  const float h = __expf(-0.5f * __builtin_fabsf(g));
+  const float a = g >= 0.0f ? 1.0f : h;
+  return ((g * a) * a) * __builtin_amdgcn_rcpf(1.0f + h * h) * u;
+}
+
+// One output of a gate_up GEMM with the activation fused: the gate and up
+// sums are each rounded to bf16 first, as the unfused GEMM stores them, so
+// the result equals the activation kernel applied to the unfused output.
+__device__ __forceinline__ uint16_t fused_silu_mul(float g, float u) {
+  const float gb = __uint_as_float(pack_bf16x2(g, 0.f) << 16);
+  const float ub = __uint_as_float(pack_bf16x2(u, 0.f) << 16);
+  return (uint16_t)(pack_bf16x2(silu_mul(gb, ub), 0.f) & 0xFFFFu);
+}
+
 struct GemmParams {
   const uint16_t* a;
   const uint8_t* wpk;
@@ -318,6 +350,7 @@ struct GemmParams {
   int32_t* work;            // dynamic schedule: work counter (workspace)
   int32_t wg_log2;          // packed layout: log2 of the tiles per block group
   int32_t fold;             // column-block groups per tile dealt to the XCDs (divides nblocks)
+  int32_t act;              // 1: gate_up with silu(gate) * up fused; output row stride N / 2
 };
 
 // Place of 16-column tile t0 + j, K chunk c inside one expert's packed
@@ -735,8 +768,28 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
       p.c[(size_t)ri.out_row * p.N + n] = (uint16_t)(pack_bf16x2(v * t, 0.f) & 0xFFFFu);
     }
   };
+  // fused activation: tiles nt (gate) and nt + 1 (up) of a pair
+  auto store_pair = [&](int nt, int tm, int r, float g, float u) {
+    const RowInfo ri = row_info(p, tile, e, tm * 16 + kb * 4 + r);
+    if (!ri.valid) return;
+    const float t = (p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+    p.c[(size_t)ri.out_row * (p.N / 2) + ((nt0 + nt) / 2) * 16 + col] =
+        fused_silu_mul(g * t, u * t);
+  };
+  const bool fused = p.act && p.split == 1;
 
   if constexpr (WK == 1) {
+    if (fused) {
+      if constexpr (NTW % 2 == 0) {
+#pragma unroll
+        for (int nt = 0; nt < NTW; nt += 2)
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) store_pair(nt, tm, r, acc[nt][tm][r], acc[nt + 1][tm][r]);
+      }
+      return;
+    }
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
@@ -752,6 +805,27 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
         for (int r = 0; r < 4; ++r)
           s_red[(w * NACC + (nt * TM + tm) * 4 + r) * 64 + lane] = acc[nt][tm][r];
     __syncthreads();
+    if (fused) {
+      // wave (wk, wn) finishes tile pairs wk, wk + WK, ... of its group
+      if constexpr (NTW % 2 == 0) {
+        for (int pr = wk; pr < NTW / 2; pr += WK) {
+#pragma unroll
+          for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int ig = (2 * pr * TM + tm) * 4 + r, iu = ((2 * pr + 1) * TM + tm) * 4 + r;
+              float g = 0.f, u = 0.f;
+#pragma unroll
+              for (int j = 0; j < WK; ++j) {
+                g += s_red[((wn * WK + j) * NACC + ig) * 64 + lane];
+                u += s_red[((wn * WK + j) * NACC + iu) * 64 + lane];
+              }
+              store_pair(2 * pr, tm, r, g, u);
+            }
+        }
+      }
+      return;
+    }
     // wave (wk, wn) finishes tiles nt = wk, wk + WK, ... of its column group
     for (int nt = wk; nt < NTW; nt += WK) {
 #pragma unroll
@@ -901,17 +975,31 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
     }
     if (++c_c == KC) {
       // column block c_nb complete: lane holds rows 4*kb + r of column col
+      if (p.act) {
 #pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
+        for (int nt = 0; nt < NTW; nt += 2) {
+          const int n = (((c_nb * 4 + w) * NTW + nt) / 2) * 16 + col;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          if (out_row[r] >= 0)
-            p.c[(size_t)out_row[r] * p.N + n] =
-                (uint16_t)(pack_bf16x2(acc[nt][r] * tw[r], 0.f) & 0xFFFFu);
-          acc[nt][r] = 0.f;
+          for (int r = 0; r < 4; ++r)
+            if (out_row[r] >= 0)
+              p.c[(size_t)out_row[r] * (p.N / 2) + n] =
+                  fused_silu_mul(acc[nt][r] * tw[r], acc[nt + 1][r] * tw[r]);
+        }
+      } else {
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          const int n = ((c_nb * 4 + w) * NTW + nt) * 16 + col;
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (out_row[r] >= 0)
+              p.c[(size_t)out_row[r] * p.N + n] =
+                  (uint16_t)(pack_bf16x2(acc[nt][r] * tw[r], 0.f) & 0xFFFFu);
         }
       }
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[nt][r] = 0.f;
       c_c = 0;
       ++c_nb;
     }
@@ -1222,6 +1310,23 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   __syncthreads();
 
   // Output: lane holds rows tm*16 + 4*kb + r of column col of each tile.
+  if (p.act && p.split == 1) {
+    // fused activation: tiles nt (gate) and nt + 1 (up) of each pair
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      const i32x4 orow = *(const i32x4*)(s_orow + tm * 16 + kb * 4);
+      const f32x4 twv = *(const f32x4*)(s_tw + tm * 16 + kb * 4);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (orow[r] < 0) continue;
+#pragma unroll
+        for (int nt = 0; nt < NTW; nt += 2)
+          p.c[(size_t)orow[r] * (p.N / 2) + ((nt0 + w * NTW + nt) / 2) * 16 + col] =
+              fused_silu_mul(acc[nt][tm][r] * twv[r], acc[nt + 1][tm][r] * twv[r]);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int tm = 0; tm < TM; ++tm) {
     const i32x4 orow = *(const i32x4*)(s_orow + tm * 16 + kb * 4);
@@ -1345,6 +1450,40 @@ int scratch_device_ptr(void** out) {
 }
 
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
+  if (p.act) {
+    // fused activation: four outputs h[row, o0 .. o0+3] per thread, from
+    // gate columns 32 q + c .. and up columns 32 q + 16 + c .. of the
+    // partials (q = o0 / 16, c = o0 % 16)
+    const int64_t per_row = p.N / 8;
+    const int64_t total = (int64_t)p.num_tiles * p.BM * per_row;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+         i += (int64_t)gridDim.x * blockDim.x) {
+      const int pos = (int)(i / per_row);
+      const int o0 = (int)(i - (int64_t)pos * per_row) * 4;
+      const int tile = pos / p.BM;
+      const int e = tile_expert(p, tile);
+      if (e < 0) continue;
+      const RowInfo ri = row_info(p, tile, e, pos - tile * p.BM);
+      if (!ri.valid) continue;
+      const int ng = (o0 >> 4) * 32 + (o0 & 15);
+      float4 g = {0.f, 0.f, 0.f, 0.f}, u = {0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < p.split; ++k) {
+        const float* row = p.ws + ((size_t)k * p.rows_cap + ri.out_row) * p.N;
+        const float4 a = *(const float4*)(row + ng);
+        const float4 b = *(const float4*)(row + ng + 16);
+        g.x += a.x; g.y += a.y; g.z += a.z; g.w += a.w;
+        u.x += b.x; u.y += b.y; u.z += b.z; u.w += b.w;
+      }
+      const float t = (p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+      u32x2 o;
+      o.x = (uint32_t)fused_silu_mul(g.x * t, u.x * t) |
+            ((uint32_t)fused_silu_mul(g.y * t, u.y * t) << 16);
+      o.y = (uint32_t)fused_silu_mul(g.z * t, u.z * t) |
+            ((uint32_t)fused_silu_mul(g.w * t, u.w * t) << 16);
+      *(u32x2*)(p.c + (size_t)ri.out_row * (p.N / 2) + o0) = o;
+    }
+    return;
+  }
   const int64_t per_row = p.N / 4;
   const int64_t total = (int64_t)p.num_tiles * p.BM * per_row;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -1654,14 +1793,36 @@ __global__ __launch_bounds__(256, 2) void gemm_large_m_kernel(const GemmParams p
             }
           }
       __syncthreads();
-      const int u = threadIdx.x & 31;
+      if (p.act) {
+        // fused activation: 128 outputs per row, 8 per thread; output unit
+        // v takes 16-byte units 4 (v/2) + v%2 (gate) and that + 2 (up) of
+        // the staged row
+        const int v = threadIdx.x & 15;
+        const int ug = 4 * (v >> 1) + (v & 1);
 #pragma unroll 4
-      for (int it = 0; it < BMA / 8; ++it) {
-        const int R = it * 8 + (threadIdx.x >> 5);
-        const int out = s_out[R];
-        const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
-        const u32x4 v = *(const u32x4*)(row + ((u ^ (R & 15)) << 4));
-        if (out >= 0) *(u32x4*)(p.c + (size_t)out * p.N + nb * kLmBN + u * 8) = v;
+        for (int it = 0; it < BMA / 16; ++it) {
+          const int R = it * 16 + (threadIdx.x >> 4);
+          const int out = s_out[R];
+          const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+          const u32x4 gv = *(const u32x4*)(row + ((ug ^ (R & 15)) << 4));
+          const u32x4 uv = *(const u32x4*)(row + (((ug + 2) ^ (R & 15)) << 4));
+          u32x4 o;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            o[q] = (uint32_t)(pack_bf16x2(silu_mul(bf16_lo(gv[q]), bf16_lo(uv[q])),
+                                          silu_mul(bf16_hi(gv[q]), bf16_hi(uv[q]))));
+          if (out >= 0) *(u32x4*)(p.c + (size_t)out * (p.N / 2) + nb * (kLmBN / 2) + v * 8) = o;
+        }
+      } else {
+        const int u = threadIdx.x & 31;
+#pragma unroll 4
+        for (int it = 0; it < BMA / 8; ++it) {
+          const int R = it * 8 + (threadIdx.x >> 5);
+          const int out = s_out[R];
+          const uint8_t* row = R < BM / 2 ? &s_a0[R * 512] : &s_a1[(R - BM / 2) * 512];
+          const u32x4 v = *(const u32x4*)(row + ((u ^ (R & 15)) << 4));
+          if (out >= 0) *(u32x4*)(p.c + (size_t)out * p.N + nb * kLmBN + u * 8) = v;
+        }
       }
     } else {
       // fp32 partial sums: passes of up to BM/2 rows of 256 columns (1 KiB)
@@ -2258,6 +2419,7 @@ int launch_gemm(const GemmArgs& g, void* stream) {
   gp.KC = (int32_t)L.k_chunks;
   gp.BM = pl.block_m;
   gp.wg_log2 = L.wg_log2;
+  gp.act = L.act;
   gp.fold = 1;
   const int64_t tiles_pad = (g.num_tiles + 7) / 8 * 8;
   const int64_t grid = tiles_pad * gp.nblocks * gp.split;
@@ -2380,15 +2542,6 @@ int launch_gemm(const GemmArgs& g, void* stream) {
 // silu_and_mul: y[r, j] = silu(x[r, j]) * x[r, I + j] in fp32 ([announce]
 // measurement section: the activation between gate/up and down).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float silu_mul(float g, float u) {
-  // silu(g) = g * sigmoid(g). For g >= 0: g / (1 + e^-g). For g < 0, e^-g
-  // overflows fp32 below -88.7 while silu(g) is still a normal number, so
-  // e^g is taken in two halves h = e^(g/2): silu(g) = ((g h) h) / (1 + h h),
-  // with no intermediate overflow or premature underflow.
-  if (g >= 0.0f) return g / (1.0f + __expf(-g)) * u;
-  const float h = __expf(0.5f * g);
-  return ((g * h) * h) / (1.0f + h * h) * u;
-}
 
 __global__ __launch_bounds__(256) void silu_mul_vec8_kernel(const uint16_t* __restrict__ x,
                                                             uint16_t* __restrict__ y, int64_t R,

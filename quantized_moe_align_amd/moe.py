@@ -39,11 +39,12 @@ class ExpertWeights:
     """One projection's experts: the layer handle and its prepacked weights."""
 
     def __init__(self, qweight: np.ndarray, scales: np.ndarray, path: int = qma.PATH_INDEXED,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, flags: int = 0):
         E, N, K8 = qweight.shape
         self.E, self.N, self.K = E, N, K8 * 8
-        self.path = path
-        self.layer = qma.qma_layer_create(E, N, self.K, path)
+        self.path, self.flags = path, flags
+        self.fused = bool(flags & qma.LAYER_FUSE_SILU_MUL)
+        self.layer = qma.qma_layer_create(E, N, self.K, path, flags=flags)
         nbytes = qma.qma_packed_weight_bytes(self.layer)
         self.packed = torch.empty(nbytes, dtype=torch.uint8, device=device)
         qw = to_device(qweight, device)
@@ -58,7 +59,8 @@ class ExpertWeights:
         again)."""
         other = ExpertWeights.__new__(ExpertWeights)
         other.E, other.N, other.K, other.path = self.E, self.N, self.K, path
-        other.layer = qma.qma_layer_create(self.E, self.N, self.K, path)
+        other.flags, other.fused = self.flags, self.fused
+        other.layer = qma.qma_layer_create(self.E, self.N, self.K, path, flags=self.flags)
         if qma.qma_packed_weight_bytes(other.layer) != self.packed.numel():
             raise ValueError("packed sizes differ between paths")
         other.packed = self.packed
@@ -110,7 +112,9 @@ class Routing:
 class IndexedMoE:
     """gate_up -> silu_and_mul -> down over the indexed path for one batch
     shape (T tokens, top-k). Buffers are allocated once, so forward() only
-    enqueues kernels and can be captured in a hipGraph."""
+    enqueues kernels and can be captured in a hipGraph. With a fused gate_up
+    layer (ExpertWeights(..., flags=LAYER_FUSE_SILU_MUL)) gate_up writes the
+    activation h itself and act() enqueues nothing."""
 
     def __init__(self, w13: ExpertWeights, w2: ExpertWeights, T: int, topk: int,
                  force_block_m: int = 0, extra_cap: int = 0, device="cuda"):
@@ -129,7 +133,8 @@ class IndexedMoE:
         self.routing = Routing(torch.empty(cap, dtype=torch.int32, device=dev),
                                torch.empty(blocks, dtype=torch.int32, device=dev),
                                torch.empty(1, dtype=torch.int32, device=dev), cap, bm)
-        self.c1 = empty_bf16(max(R, 1), 2 * self.I, device=dev)
+        self.fused = w13.fused
+        self.c1 = None if self.fused else empty_bf16(max(R, 1), 2 * self.I, device=dev)
         self.h = empty_bf16(max(R, 1), self.I, device=dev)
         self.c2 = empty_bf16(max(R, 1), self.K, device=dev)
         self.ws13 = workspace_for(self.plan13, dev)
@@ -158,11 +163,12 @@ class IndexedMoE:
         r = self.routing
         qma.qma_indexed_gemm(self.w13.layer, self.plan13, a, self.T, self.topk,
                              self.w13.packed, r.sorted_ids, r.expert_ids, r.ntp, r.cap,
-                             self.T * self.topk, None, self.c1, self.ws13,
-                             0 if self.ws13 is None else self.ws13.numel(), stream)
+                             self.T * self.topk, None, self.h if self.fused else self.c1,
+                             self.ws13, 0 if self.ws13 is None else self.ws13.numel(), stream)
 
     def act(self, stream=None):
-        qma.qma_silu_and_mul(self.c1, self.h, self.T * self.topk, self.I, stream)
+        if not self.fused:
+            qma.qma_silu_and_mul(self.c1, self.h, self.T * self.topk, self.I, stream)
 
     def down(self, topk_weights: Optional[torch.Tensor] = None, stream=None):
         r = self.routing
@@ -195,7 +201,8 @@ class GroupedMoE:
         self.plan2 = qma.qma_plan_grouped(w2.layer, rows_or_budget, expected_m)
         rows = rows_or_budget * (self.E if self.masked else 1)
         self.rows = rows
-        self.c1 = empty_bf16(max(rows, 1), 2 * self.I, device=device)
+        self.fused = w13.fused
+        self.c1 = None if self.fused else empty_bf16(max(rows, 1), 2 * self.I, device=device)
         self.h = empty_bf16(max(rows, 1), self.I, device=device)
         self.c2 = empty_bf16(max(rows, 1), self.K, device=device)
         self.ws13 = workspace_for(self.plan13, device)
@@ -225,10 +232,12 @@ class GroupedMoE:
         return tuple(done)
 
     def gate_up(self, a, index, stream=None):
-        self._gemm(self.w13, self.plan13, a, self.c1, self.ws13, index, stream)
+        self._gemm(self.w13, self.plan13, a, self.h if self.fused else self.c1, self.ws13, index,
+                   stream)
 
     def act(self, stream=None):
-        qma.qma_silu_and_mul(self.c1, self.h, self.rows, self.I, stream)
+        if not self.fused:
+            qma.qma_silu_and_mul(self.c1, self.h, self.rows, self.I, stream)
 
     def down(self, index, stream=None):
         self._gemm(self.w2, self.plan2, self.h, self.c2, self.ws2, index, stream)

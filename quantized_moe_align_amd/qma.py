@@ -16,6 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqma.so")
 
 SCHEDULE_SEMI_STATIC, SCHEDULE_DYNAMIC, SCHEDULE_GANG = 0, 1, 2
+LAYER_FUSE_SILU_MUL = 1
 SCHEDULE_NAMES = {0: "semi_static", 1: "dynamic", 2: "gang"}
 
 QMA_OK, QMA_ERR_INVALID_ARG, QMA_ERR_UNSUPPORTED, QMA_ERR_ROUTING, \
@@ -29,7 +30,7 @@ PROFILES = {0: "generic", 1: "ep_gate_up", 2: "ep_down", 3: "tp_gate_up", 4: "tp
 
 # Every symbol include/qma.h declares.
 EXPORTS = (
-    "qma_layer_create", "qma_layer_destroy", "qma_layer_info",
+    "qma_layer_create", "qma_layer_create_ex", "qma_layer_destroy", "qma_layer_info",
     "qma_packed_weight_bytes", "qma_prepack", "qma_plan_indexed",
     "qma_plan_grouped", "qma_workspace_bytes", "qma_align_sizes",
     "qma_moe_align", "qma_validate_routing", "qma_validate_contiguous",
@@ -84,6 +85,8 @@ def lib():
         sig = {
             "qma_layer_create": (I32, [ctypes.POINTER(QuantDesc), I32, I32, I32, I32,
                                        ctypes.POINTER(P)]),
+            "qma_layer_create_ex": (I32, [ctypes.POINTER(QuantDesc), I32, I32, I32, I32,
+                                          ctypes.c_uint32, ctypes.POINTER(P)]),
             "qma_layer_destroy": (None, [P]),
             "qma_layer_info": (I32, [P] + [ctypes.POINTER(I32)] * 5),
             "qma_packed_weight_bytes": (SZ, [P]),
@@ -148,10 +151,14 @@ def qma_version() -> str:
 
 
 def qma_layer_create(E: int, N: int, K: int, path: int = PATH_INDEXED,
-                     desc: Optional[QuantDesc] = None) -> ctypes.c_void_p:
+                     desc: Optional[QuantDesc] = None, flags: int = 0) -> ctypes.c_void_p:
     out = ctypes.c_void_p()
-    _check(lib().qma_layer_create(ctypes.byref(desc or w4a16_desc()), E, N, K, path,
-                                  ctypes.byref(out)))
+    if flags:
+        _check(lib().qma_layer_create_ex(ctypes.byref(desc or w4a16_desc()), E, N, K, path,
+                                         flags, ctypes.byref(out)))
+    else:
+        _check(lib().qma_layer_create(ctypes.byref(desc or w4a16_desc()), E, N, K, path,
+                                      ctypes.byref(out)))
     return out
 
 

@@ -34,14 +34,17 @@ def apply_override(plan, override):
 
 
 def indexed(a_bits, a_row_div, ids, w, s, *, T=None, topk=None, force_bm=0, override=None,
-            extra_cap=0, junk_tail=False, topk_w=None, pre=None):
-    """Run moe_align + one indexed GEMM through the ABI; return output bits."""
+            extra_cap=0, junk_tail=False, topk_w=None, pre=None, flags=0):
+    """Run moe_align + one indexed GEMM through the ABI; return output bits
+    ([R, N], or [R, N / 2] for a layer with the activation fused)."""
     E, N, K8 = w.shape
     ids = np.asarray(ids, np.int32)
     T = ids.shape[0] if T is None else T
     topk = ids.shape[1] if topk is None else topk
     R = T * topk
-    W = ExpertWeights(w, s)
+    W = ExpertWeights(w, s, flags=flags)
+    if W.fused:
+        N //= 2
     plan = qma.qma_plan_indexed(W.layer, T, topk, force_bm)
     apply_override(plan, override)
     B = plan.block_m
@@ -223,9 +226,11 @@ def test_permutation_equivariance_bitwise(gpu):
 
 # ---- grouped paths -------------------------------------------------------
 
-def contiguous(a_bits, m_idx, w, s, override=None):
+def contiguous(a_bits, m_idx, w, s, override=None, flags=0):
     E, N, K8 = w.shape
-    W = ExpertWeights(w, s, qma.PATH_GROUPED_CONTIGUOUS)
+    W = ExpertWeights(w, s, qma.PATH_GROUPED_CONTIGUOUS, flags=flags)
+    if W.fused:
+        N //= 2
     M = m_idx.size
     plan = qma.qma_plan_grouped(W.layer, M, 0)
     apply_override(plan, override)
@@ -237,10 +242,12 @@ def contiguous(a_bits, m_idx, w, s, override=None):
     return to_host(c, bf16=True)
 
 
-def masked(a_bits, masked_m, expected_m, w, s, override=None):
+def masked(a_bits, masked_m, expected_m, w, s, override=None, flags=0):
     E, N, K8 = w.shape
     Eb, Mb, K = a_bits.shape
-    W = ExpertWeights(w, s, qma.PATH_GROUPED_MASKED)
+    W = ExpertWeights(w, s, qma.PATH_GROUPED_MASKED, flags=flags)
+    if W.fused:
+        N //= 2
     plan = qma.qma_plan_grouped(W.layer, Mb, expected_m)
     apply_override(plan, override)
     c = torch.full((E, Mb, N), SENT, dtype=torch.int16, device="cuda")
@@ -821,6 +828,81 @@ def test_gang_schedule_with_nothing_routed(gpu):
                                   "schedule": qma.SCHEDULE_GANG})
     assert plan.schedule == qma.SCHEDULE_GANG
     assert np.all(got == SENT)
+
+
+# Gate_up with the activation fused: h = silu(gate) * up from the GEMM's own
+# epilogue (or split-K reduction) equals the activation kernel applied to the
+# unfused output, bit for bit, on every kernel family a gate_up plan can take.
+def silu_of(c_bits):
+    """The library's activation kernel on an unfused gate_up output."""
+    R, N = c_bits.shape
+    x = to_device(c_bits)
+    h = torch.empty((R, N // 2), dtype=torch.int16, device="cuda")
+    qma.qma_silu_and_mul(x, h, R, N // 2)
+    torch.cuda.synchronize()
+    return to_host(h, bf16=True)
+
+
+FUSED_PLANS = [
+    ({"block_m": 16, "block_n": 128, "waves_k": 1}, 1024),
+    ({"block_m": 16, "block_n": 256, "waves_k": 1, "schedule": qma.SCHEDULE_GANG}, 1024),
+    ({"block_m": 32, "block_n": 256, "waves_k": 1, "schedule": qma.SCHEDULE_DYNAMIC}, 1024),
+    ({"block_m": 64, "block_n": 128, "waves_k": 1}, 1024),
+    ({"block_m": 16, "block_n": 128, "waves_k": 2}, 1024),
+    ({"block_m": 16, "block_n": 64, "waves_k": 4}, 1024),
+    ({"block_m": 16, "block_n": 128, "waves_k": 1, "split_k": 3}, 1024),
+    ({"block_m": 16, "block_n": 64, "waves_k": 4, "split_k": 2}, 1024),
+    ({"block_m": 16, "block_n": 256, "waves_k": 1, "n_stream": 3}, 256),
+    ({"kernel": qma.KERNEL_LARGE_M, "block_m": 128, "block_n": 256}, 512),
+    ({"kernel": qma.KERNEL_LARGE_M, "block_m": 128, "block_n": 256, "split_k": 2}, 512),
+]
+
+
+@pytest.mark.parametrize("case", range(len(FUSED_PLANS)))
+def test_fused_activation_matches_unfused(gpu, case):
+    ov, K = FUSED_PLANS[case]
+    ov = dict({"kernel": qma.KERNEL_SMALL_M, "split_k": 1, "n_stream": 1}, **ov)
+    large = ov["kernel"] == qma.KERNEL_LARGE_M
+    E, T, topk, N = 6, 420 if large else 150, 2, 1536
+    rng = np.random.default_rng(380 + case)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    tw = rng.random(T * topk).astype(np.float32)
+    bm = ov["block_m"]
+    plain, _ = indexed(a, topk, ids, w, s, force_bm=bm, override=ov)
+    fused, plan = indexed(a, topk, ids, w, s, force_bm=bm, override=ov,
+                          flags=qma.LAYER_FUSE_SILU_MUL)
+    assert plan.kernel == ov["kernel"] and plan.split_k == ov["split_k"]
+    valid = slot_experts(ids, E) >= 0
+    ref = silu_of(plain)
+    assert np.array_equal(fused[valid], ref[valid])
+    assert np.all(fused[~valid] == SENT)
+    # and the oracle's activation of the same gate_up output, within one bf16 ulp
+    h64 = O.silu_and_mul(plain[valid])
+    ulp = np.abs(O.bf16_to_f64(rne(h64)) * 2.0 ** -7) + 2.0 ** -126
+    assert np.all(np.abs(O.bf16_to_f64(fused[valid]) - h64) <= ulp)
+
+
+def test_fused_activation_grouped(gpu):
+    E, K, N = 5, 512, 1024
+    rng = np.random.default_rng(395)
+    w, s = weights(rng, E, N, K)
+    wl = inputs.make_contiguous("c", 6, E, 0, K, N // 2, counts=[200, 0, 70, 128, 33],
+                                weights=False)
+    m_idx = wl["m_indices"]
+    got = contiguous(wl["a"], m_idx, w, s, flags=qma.LAYER_FUSE_SILU_MUL)
+    ref = silu_of(contiguous(wl["a"], m_idx, w, s))
+    assert np.array_equal(got[m_idx >= 0], ref[m_idx >= 0])
+    Mb = 64
+    masked_m = np.array([32, 0, 64, 1, 17], np.int32)
+    am = inputs.bf16_normal(rng, (E, Mb, K))
+    got_m = masked(am, masked_m, 32, w, s, flags=qma.LAYER_FUSE_SILU_MUL)
+    plain_m = masked(am, masked_m, 32, w, s)
+    ref_m = silu_of(plain_m.reshape(E * Mb, N)).reshape(E, Mb, N // 2)
+    row_e = np.array([[r < masked_m[e] for r in range(Mb)] for e in range(E)])
+    assert np.array_equal(got_m[row_e], ref_m[row_e])
+    assert np.all(got_m[~row_e] == SENT)
 
 
 # ---- degenerate routing: nothing to compute --------------------------------

@@ -118,3 +118,41 @@ def test_grouped_workload(gpu, name):
     c1, h, c2 = (to_host(t, bf16=True) for t in (moe.c1, moe.h, moe.c2))
     check_stages(a_rows, 1, row_e, c1, h, c2, wl["w13"], wl["s13"], wl["w2"], wl["s2"], rng,
                  name, full=name not in PREFILL)
+
+
+@pytest.mark.parametrize("name", ["ep8_decode", "tp8", "ep128_decode", "ep32_decode", "ep8_prefill",
+                                  "contiguous", "masked"])
+def test_fused_activation_full_size(gpu, name):
+    """gate_up with the activation fused (the benchmark's default step) gives
+    the unfused gate_up + activation kernel's h bit for bit, and the same
+    down output, at the workload's full size and with the planner's plans."""
+    wl = inputs.make(name, seed=0)
+    outs = {}
+    for flags in (0, qma.LAYER_FUSE_SILU_MUL):
+        if wl.kind == "indexed":
+            moe = IndexedMoE(ExpertWeights(wl["w13"], wl["s13"], flags=flags),
+                             ExpertWeights(wl["w2"], wl["s2"]), wl.T, wl.topk)
+            moe.forward(to_device(wl["a"]), to_device(wl["topk_ids"]))
+            valid = slot_experts(wl["topk_ids"], wl.E) >= 0
+        else:
+            path = (qma.PATH_GROUPED_CONTIGUOUS if wl.kind == "contiguous"
+                    else qma.PATH_GROUPED_MASKED)
+            w13 = ExpertWeights(wl["w13"], wl["s13"], path, flags=flags)
+            w2 = ExpertWeights(wl["w2"], wl["s2"], path)
+            if wl.kind == "contiguous":
+                index = wl["m_indices"]
+                moe = GroupedMoE(w13, w2, index.size)
+                valid = index >= 0
+            else:
+                index = wl["masked_m"]
+                budget = wl.meta["budget"]
+                moe = GroupedMoE(w13, w2, budget, wl.meta["expected_m"])
+                valid = np.array([[r < index[e] for r in range(budget)]
+                                  for e in range(wl.E)]).reshape(-1)
+            moe.forward(to_device(wl["a"]), to_device(index))
+        torch.cuda.synchronize()
+        assert moe.fused == bool(flags)
+        outs[flags] = (to_host(moe.h, bf16=True)[valid], to_host(moe.c2, bf16=True)[valid])
+        del moe
+    assert np.array_equal(outs[0][0], outs[qma.LAYER_FUSE_SILU_MUL][0]), f"{name} h"
+    assert np.array_equal(outs[0][1], outs[qma.LAYER_FUSE_SILU_MUL][1]), f"{name} down"

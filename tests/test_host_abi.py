@@ -61,6 +61,43 @@ def test_bad_shapes(L, E, N, K):
     assert ei.value.status == qma.QMA_ERR_INVALID_ARG
 
 
+def test_fused_activation_layer_rules(L):
+    F = qma.LAYER_FUSE_SILU_MUL
+    # unknown flag bits and widths that cannot pair gate and up tiles per wave
+    for N, flags in ((4096, 2), (4096, F | 4), (4064, F), (96, F)):
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_layer_create(8, N, 1024, flags=flags)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG, (N, flags)
+    lay = qma.qma_layer_create(48, 4096, 7168, flags=F)
+    try:
+        # the planner's plans give every wave gate/up pairs
+        for T in (12, 576, 48 * 40, 8192):
+            p = qma.qma_plan_indexed(lay, T, 1, 0)
+            if p.kernel == qma.KERNEL_SMALL_M:
+                assert (p.block_n // (16 * (4 // p.waves_k))) % 2 == 0, T
+        # the same packed size as the unfused layer (only the tile order differs)
+        plain = qma.qma_layer_create(48, 4096, 7168)
+        assert qma.qma_packed_weight_bytes(plain) == qma.qma_packed_weight_bytes(lay)
+        qma.qma_layer_destroy(plain)
+        # host checks before any launch: one tile per wave, and the
+        # producer/consumer kernel, have no fused epilogue
+        fake = 1 << 20                     # rejected on the host; never dereferenced
+        p = qma.qma_plan_indexed(lay, 12, 1, 16)
+        p.block_n, p.waves_k, p.split_k, p.schedule = 16, 4, 1, 0
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_indexed_gemm(lay, p, fake, 12, 1, fake, fake, fake, fake, 12 + 15, 12,
+                                 None, fake, stream=0)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG and "even" in ei.value.detail
+        q = qma.qma_plan_indexed(lay, 48 * 100, 1, 128)
+        q.kernel, q.split_k = qma.KERNEL_LARGE_M_PC, 1
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_indexed_gemm(lay, q, fake, 4800, 1, fake, fake, fake, fake, 4800 + 48 * 127,
+                                 4800, None, fake, stream=0)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG and "fused" in ei.value.detail
+    finally:
+        qma.qma_layer_destroy(lay)
+
+
 def test_per_expert_weights_must_fit_32_bit_offsets(L):
     # kernels address one expert's packed blocks with 32-bit offsets: N x K / 2
     # bytes of nibbles must stay below 2 GiB (65536 x 65536 / 2 = 2 GiB exactly)
