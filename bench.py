@@ -664,6 +664,7 @@ def main():
         "algorithmic": work,
         "plan": headline_plan,
         "roofline": roof,
+        "kernel_src_sha": kernel_src_hash(),
     }
 
     # every scenario of the pages, measured in the same run
