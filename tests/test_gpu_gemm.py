@@ -510,6 +510,37 @@ def test_graph_capture_replays_match_eager(gpu):
         assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
 
 
+def test_graph_capture_fused_gang(gpu):
+    # the default decode step's pieces in one graph: gate_up with the
+    # activation fused and both GEMMs on the gang schedule (dynamic LDS,
+    # persistent groups), replayed against the eager result
+    wl = inputs.make("tiny", seed=3)
+    moe = IndexedMoE(ExpertWeights(wl["w13"], wl["s13"], flags=qma.LAYER_FUSE_SILU_MUL),
+                     ExpertWeights(wl["w2"], wl["s2"]), wl.T, wl.topk)
+    assert moe.set_schedule(qma.SCHEDULE_GANG) == (True, True)
+    a = to_device(wl["a"])
+    ids = to_device(wl["topk_ids"])
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        moe.forward(a, ids)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    eager = to_host(moe.c2, bf16=True).copy()
+    h_eager = to_host(moe.h, bf16=True).copy()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.forward(a, ids)
+    for i in range(4):
+        moe.c2.fill_(0)
+        moe.h.fill_(0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(to_host(moe.h, bf16=True), h_eager), f"replay {i} h"
+        assert np.array_equal(to_host(moe.c2, bf16=True), eager), f"replay {i}"
+
+
 def test_graph_capture_large_m_split_k(gpu):
     # the large-M kernel with split-K (fp32 partials in the workspace, then
     # the reduce kernel) for both projections, captured and replayed
