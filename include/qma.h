@@ -246,12 +246,12 @@ qma_status qma_prepack(const qma_layer_t* layer, const int32_t* qweight,
  * block-M heuristic keyed on routed tokens per expert, switching at 80),
  * block_n comes from the tile count ([release] grouped techniques: the
  * wider tile only when enough N tiles exist, never below 128 columns with
- * long K), and split-K turns on only when the grid would underfill the
- * compute units ([release] indexed techniques: the stream-K gate); it then
- * aims at 1.5 workgroups per compute unit and keeps at least 14 K chunks
- * of 128 per split. Between one and two workgroups per compute unit with
- * long K, 16-row tiles split K across wave pairs inside the workgroup
- * (waves_k = 2) instead. Plans whose items fill one round of the gang
+ * long K), and split-K turns on only when the grid would hold fewer than
+ * two workgroups per compute unit ([release] indexed techniques: the
+ * stream-K gate); it then aims at three per compute unit and keeps at
+ * least 14 K chunks of 128 per split. An underfilled grid whose K is too
+ * short to split takes 64-column blocks with the waves on K (waves_k = 4)
+ * instead. Plans whose items fill one round of the gang
  * schedule take it (QMA_SCHEDULE_GANG, with its width rule); the others
  * are semi-static. force_block_m = 0 lets the planner choose;
  * otherwise 16, 32 or 64 selects the small-M kernel with that tile and 128

@@ -102,18 +102,6 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     if (tm == 1 && ntw == 2 && L.k_chunks >= 4 * qma::kStreamChunks && L.N % 256 == 0 &&
         L.N / 256 >= 8 && (int64_t)tiles_m * (L.N / 256) >= 3 * qma::kNumCUs)
       ntw = 4;
-    // Between one and two workgroups per CU with long K (an EP32 gate_up
-    // share: 384 tiles), two wave pairs splitting K keep more weight loads in
-    // flight per workgroup than four waves side by side (measured 52 vs
-    // 60 us). At three chunks in flight per wave this ran 50.5-50.8 us,
-    // against 52.0 us at four and 51.6-51.8 us for the shared-row kernel
-    // with split-K 2 (same box).
-    const int64_t t128 = L.N % 128 == 0 ? (int64_t)tiles_m * (L.N / 128) : 0;
-    if (tm == 1 && L.k_chunks >= 4 * qma::kStreamChunks && t128 >= qma::kNumCUs &&
-        t128 < 2 * qma::kNumCUs) {
-      wk = 2;
-      ntw = 4;
-    }
   } else {
     // 64-row tiles: the shared-row kernel at 128 columns (four waves side by
     // side, two column tiles each), its rows staged once per workgroup; an
@@ -132,16 +120,20 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   const int32_t tiles =
       (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / p->block_n), 1 << 30);
   p->est_tiles = tiles;
-  // Split-K gate: only when the grid underfills the CUs. It then aims at
-  // 1.5 workgroups per CU, never below kSplitChunks 128-wide K chunks per
-  // split. (EP128 gate_up, 96 tiles, K = 56 chunks: split 2/3/4/6/8 ran
+  // Split-K gate: only when the grid holds fewer than two workgroups per
+  // CU. It then aims at three per CU (one round of the gang schedule),
+  // never below kSplitChunks 128-wide K chunks per split. (An EP32 gate_up
+  // share, 384 tiles: split 2 on the shared-row kernel ran 42.1 us, 41.2 us
+  // as a gang, against 48.0 us for two wave pairs splitting K inside the
+  // workgroup, the earlier rule for one to two workgroups per CU; before
+  // the tiles were folded over the XCDs that order was reversed.) (EP128 gate_up, 96 tiles, K = 56 chunks: split 2/3/4/6/8 ran
   // 29.9/25.6/23.0/22.5/22.0 us with the tiles folded over all XCDs, 1: 45 us;
   // down, 168 tiles, K = 16 chunks: split 2 no faster than unsplit.)
   int32_t split = 1;
-  if (tiles < qma::kNumCUs) {
+  if (tiles < 2 * qma::kNumCUs) {
     const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / qma::kSplitChunks));
     split = std::min<int32_t>(
-        {ceil_div(3 * qma::kNumCUs / 2, std::max(tiles, 1)), max_split, 8});
+        {ceil_div(qma::kGangGroups * qma::kNumCUs, std::max(tiles, 1)), max_split, 8});
     split = std::max<int32_t>(split, 1);
   }
   // An underfilled grid that K is too short to split (an EP128 down share:
@@ -160,8 +152,7 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->split_k = split;
   // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
   // chunks in flight per wave at three workgroups per CU
-  int depth = tm <= 2 && wk == 1 && split == 1 && ntw >= 2 ? 2 : qma::small_m_depth(tm, ntw);
-  if (tm == 1 && wk == 2 && split == 1) depth = 3;  // the K-split pairs above
+  const int depth = qma::small_m_shared_rows(tm, ntw, wk) ? 2 : qma::small_m_depth(tm, ntw);
   p->k_depth = depth * qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
   // only one or two chunks would spend its life on start-up and one memory
@@ -184,21 +175,23 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   // box: EP8 decode gate_up 127-129 -> 119-121 us, TP8 gate_up (256
   // columns) 129-130 -> 121-122 us, masked gate_up 157 -> 149-152 us.
   p->schedule = QMA_SCHEDULE_SEMI_STATIC;
-  if (wk == 1 && split == 1 && p->n_stream == 1 && L.k_chunks >= qma::kStreamChunks) {
+  if (wk == 1 && p->n_stream == 1 && L.k_chunks >= qma::kStreamChunks) {
     const int64_t slots = (int64_t)qma::kGangGroups * qma::kNumCUs;
-    for (const int cand : {ntw, 4, 2}) {
+    // a split plan keeps its width (its split was sized for it)
+    const int cands[3] = {ntw, split > 1 ? ntw : 4, split > 1 ? ntw : 2};
+    for (const int cand : cands) {
       if (!qma::small_m_shared_rows(tm, cand, 1) || L.N % (64 * cand) != 0) continue;
       // token tiles (folded into column-block groups where few) are dealt
       // to the 8 XCDs in turn: the fullest XCD must fit one round too (an
       // EP32 down share without folding, 12 tiles x 56 blocks, had 112 items
       // on four XCDs and ran 40.9 us this way against 28.6 us semi-static)
       const int64_t nbc = L.N / (64 * cand);
-      const int64_t items = (int64_t)tiles_m * nbc;
+      const int64_t items = (int64_t)tiles_m * nbc * split;
       const int f = qma::xcd_fold(tiles_m, nbc);
-      const int64_t per_xcd = ceil_div((int64_t)tiles_m * f, 8) * (nbc / f);
+      const int64_t per_xcd = ceil_div((int64_t)tiles_m * f, 8) * (nbc / f) * split;
       if (per_xcd > slots / 8 || 6 * items < qma::kGangMinFill * slots) continue;
       p->block_n = 64 * cand;
-      p->est_tiles = (int32_t)items;
+      p->est_tiles = (int32_t)(items / split);
       p->schedule = QMA_SCHEDULE_GANG;
       break;
     }

@@ -175,8 +175,8 @@ def test_block_m_follows_tok_e():
 
 
 def test_split_k_gate_turns_on_only_when_underfilled():
-    # 1 expert: 32 tiles at 128 columns < 256 CUs -> split toward 1.5
-    # workgroups per CU, capped at 56 / 14 = 4 K runs of 14 chunks
+    # 1 expert: 32 tiles at 128 columns, under two per CU -> split toward
+    # three workgroups per CU, capped at 56 / 14 = 4 K runs of 14 chunks
     p = _plan(1, 4096, 7168, 12, 1)
     assert p.block_n == 128 and p.est_tiles == 32 and p.split_k == 4 and p.waves_k == 1
     assert qma.qma_workspace_bytes(p) == p.split_k * 12 * 4096 * 4
@@ -187,12 +187,16 @@ def test_split_k_gate_turns_on_only_when_underfilled():
     assert g.block_n == 128 and g.est_tiles == 96 and g.split_k == 4
     d = _plan(3, 7168, 2048, 35, 1)
     assert d.block_n == 64 and d.waves_k == 4 and d.est_tiles == 336 and d.split_k == 1
-    # 8 experts: 256 tiles at 128 columns -> no split
-    assert _plan(8, 4096, 7168, 96, 1).split_k == 1
-    # EP32 share: 12 experts x 32 tiles = 384 >= 256 -> no split; between one
-    # and two workgroups per CU the waves split K in pairs (128 columns)
+    # 8 experts: 256 tiles -> split 3 (768 items, one gang round)
+    e8 = _plan(8, 4096, 7168, 96, 1)
+    assert e8.split_k == 3 and e8.schedule == qma.SCHEDULE_GANG
+    # EP32 share: 12 experts x 32 tiles = 384 -> split 2 on the shared-row
+    # kernel, one gang round of 768 items
     q = _plan(12, 4096, 7168, 144, 1)
-    assert q.split_k == 1 and q.block_n == 128 and q.waves_k == 2 and q.k_depth == 384
+    assert q.split_k == 2 and q.block_n == 128 and q.waves_k == 1 and q.k_depth == 256
+    assert q.schedule == qma.SCHEDULE_GANG
+    # 512 tiles and more (two per CU): no split
+    assert _plan(16, 4096, 7168, 192, 1).split_k == 1
     # EP32 down (672 tiles) and EP16 gate_up (768 tiles): four waves side by side
     d = _plan(12, 7168, 2048, 144, 1)
     assert d.split_k == 1 and d.block_n == 128 and d.waves_k == 1
@@ -230,8 +234,8 @@ def test_gang_schedule_plan_rules():
         assert (p.schedule == qma.SCHEDULE_GANG) == gang, (E, p.est_tiles)
     # never for short K, streaming, K split across waves, split-K or large-M
     assert _plan(384, 7168, 256, 256, 8).schedule == qma.SCHEDULE_SEMI_STATIC
-    assert _plan(12, 4096, 7168, 144, 1).schedule == qma.SCHEDULE_SEMI_STATIC   # waves_k 2
-    assert _plan(3, 4096, 7168, 36, 1).schedule == qma.SCHEDULE_SEMI_STATIC     # split-K
+    # 3 experts: split 4 gives 384 items, half a round
+    assert _plan(3, 4096, 7168, 36, 1).schedule == qma.SCHEDULE_SEMI_STATIC
     assert _plan(48, 4096, 7168, 48 * 100, 1).schedule == qma.SCHEDULE_SEMI_STATIC
     # 12 tiles folded into 24 column-block groups: 3 x 28 items per XCD
     assert _plan(12, 7168, 2048, 144, 1).schedule == qma.SCHEDULE_GANG
@@ -455,19 +459,20 @@ def test_planner_invariants_over_shapes():
             if p.n_stream > 1:                               # streaming: short K only
                 assert K // 128 < 8 and p.block_m == 16 and p.split_k == 1, shape
             if p.schedule == qma.SCHEDULE_GANG:
-                # a shared-row instance, one K partition, one round of groups
-                assert shared and p.n_stream == 1 and p.split_k == 1, shape
-                assert 640 <= p.est_tiles <= 768 and K // 128 >= 8, shape
+                # a shared-row instance with long K, one round of groups
+                assert shared and p.n_stream == 1 and K // 128 >= 8, shape
                 nb = N // p.block_n
                 tiles_m = p.est_tiles // nb
+                assert 640 <= p.est_tiles * p.split_k <= 768, shape
                 f = xcd_fold(tiles_m, nb)
-                assert -(-tiles_m * f // 8) * (nb // f) <= 96, shape
+                assert -(-tiles_m * f // 8) * (nb // f) * p.split_k <= 96, shape
             else:
                 assert p.schedule == qma.SCHEDULE_SEMI_STATIC, shape
         if p.split_k > 1:
-            # split-K only when the grid underfills the CUs, and never below
-            # 14 128-wide K chunks per split (four for large-M)
-            assert p.est_tiles < 256, shape
+            # split-K only under two workgroups per CU (small-M; large-M
+            # under one), and never below 14 128-wide K chunks per split
+            # (four for large-M)
+            assert p.est_tiles < (256 if p.kernel == qma.KERNEL_LARGE_M else 512), shape
             per_split = 4 if p.kernel == qma.KERNEL_LARGE_M else 14
             assert K // 128 >= per_split * p.split_k, shape
             assert qma.qma_workspace_bytes(p) > 0, shape
