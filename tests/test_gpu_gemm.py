@@ -999,3 +999,61 @@ def test_pipeline_depth_bit_identical(gpu, plan_i, integer):
     else:
         assert_per_expert(outs[0], ref, slot_experts(ids, E), "depth")
     assert np.all(outs[0][~valid] == SENT)
+
+
+# Randomized shapes (seeded): on each, every schedule and layout variant a
+# plan can take (the planner's own plan, the gang schedule, folds of the
+# column blocks over the XCDs, split-K, the activation fused) agrees bit for
+# bit with the semi-static, unsplit, unfused run of the same tile size, and
+# that run with the oracle (integer-exact inputs).
+def _variant_run(W, plan, a_bits, ids, T, topk, out_cols):
+    E, B = W.E, plan.block_m
+    cap = qma.qma_align_sizes(T, topk, E, B)[0]
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device="cuda")
+    expert_ids = torch.empty(-(-cap // B), dtype=torch.int32, device="cuda")
+    ntp = torch.empty(1, dtype=torch.int32, device="cuda")
+    qma.qma_moe_align(to_device(ids), T, topk, E, B, sorted_ids, expert_ids, ntp, cap)
+    R = T * topk
+    c = torch.full((R, out_cols), SENT, dtype=torch.int16, device="cuda")
+    ws = workspace_for(plan)
+    qma.qma_indexed_gemm(W.layer, plan, to_device(a_bits), T, topk, W.packed, sorted_ids,
+                         expert_ids, ntp, cap, R, None, c, ws, 0 if ws is None else ws.numel())
+    torch.cuda.synchronize()
+    return to_host(c, bf16=True)
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_randomized_plan_variants_bitwise(gpu, case):
+    rng = np.random.default_rng(900 + case)
+    E, topk, T = int(rng.integers(1, 40)), int(rng.integers(1, 4)), int(rng.integers(1, 300))
+    K = int(rng.choice([256, 512, 1024, 2048]))
+    N = int(rng.choice([256, 512, 768, 1024, 1536, 2048]))
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    plain = ExpertWeights(w, s)
+    fused = ExpertWeights(w, s, flags=qma.LAYER_FUSE_SILU_MUL)
+    base = qma.qma_plan_indexed(plain.layer, T, topk, 0)
+    bm = base.block_m
+    ref_plan = qma.qma_plan_indexed(plain.layer, T, topk, bm)
+    ref_plan.schedule = qma.SCHEDULE_SEMI_STATIC
+    if ref_plan.kernel == qma.KERNEL_SMALL_M:
+        ref_plan.split_k = 1
+    ref = _variant_run(plain, ref_plan, a, ids, T, topk, N)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(ref[valid], rne(O.moe_gemm_by_slot(a, topk, ids, w, s)[valid]))
+    h_ref = silu_of(ref)
+    variants = [{}]
+    if base.kernel == qma.KERNEL_SMALL_M:
+        nb = N // base.block_n
+        variants += [{"est_tiles": nb}, {"est_tiles": 3 * nb}, {"split_k": 2, "n_stream": 1}]
+        if base.waves_k == 1 and base.n_stream == 1 and base.block_n in (128, 256) and bm <= 32:
+            variants.append({"schedule": qma.SCHEDULE_GANG})
+    for ov in variants:
+        for W, want, cols in ((plain, ref, N), (fused, h_ref, N // 2)):
+            plan = qma.qma_plan_indexed(W.layer, T, topk, bm)
+            for k, v in ov.items():
+                setattr(plan, k, v)
+            got = _variant_run(W, plan, a, ids, T, topk, cols)
+            assert np.array_equal(got[valid], want[valid]), (ov, W.fused, plan.as_dict())
+            assert np.all(got[~valid] == SENT), (ov, W.fused)
