@@ -122,13 +122,16 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   p->est_tiles = tiles;
   // Split-K gate: only when the grid holds fewer than two workgroups per
   // CU. It then aims at three per CU (one round of the gang schedule),
-  // never below kSplitChunks 128-wide K chunks per split. (An EP32 gate_up
-  // share, 384 tiles: split 2 on the shared-row kernel ran 42.1 us, 41.2 us
-  // as a gang, against 48.0 us for two wave pairs splitting K inside the
-  // workgroup, the earlier rule for one to two workgroups per CU; before
-  // the tiles were folded over the XCDs that order was reversed.) (EP128 gate_up, 96 tiles, K = 56 chunks: split 2/3/4/6/8 ran
-  // 29.9/25.6/23.0/22.5/22.0 us with the tiles folded over all XCDs, 1: 45 us;
-  // down, 168 tiles, K = 16 chunks: split 2 no faster than unsplit.)
+  // never below kSplitChunks 128-wide K chunks per split.
+  // * An EP32 gate_up share, 384 tiles: split 2 on the shared-row kernel
+  //   ran 42.1 us, 41.2 us as a gang, against 48.0 us for two wave pairs
+  //   splitting K inside the workgroup, the earlier rule for one to two
+  //   workgroups per CU; before the tiles were folded over the XCDs that
+  //   order was reversed.
+  // * EP128 gate_up, 96 tiles, K = 56 chunks: split 2/3/4/6/8 ran
+  //   29.9/25.6/23.0/22.5/22.0 us with the tiles folded over all XCDs, and
+  //   unsplit 45 us; down, 168 tiles, K = 16 chunks: split 2 was no faster
+  //   than unsplit.
   int32_t split = 1;
   if (tiles < 2 * qma::kNumCUs) {
     const int32_t max_split = std::max<int32_t>(1, (int32_t)(L.k_chunks / qma::kSplitChunks));
@@ -138,9 +141,10 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
   }
   // An underfilled grid that K is too short to split (an EP128 down share:
   // 3 tiles x 56 blocks of 128 columns, 16 chunks) takes 64-column blocks,
-  // one column tile per wave and the waves on K, for twice the workgroups:
-  // 16.7 -> 13.2 us. (With long K, split-K stays ahead: EP128 gate_up at
-  // 64 columns and split 2 ran 21.6 us against 23.0 at 128 and split 4.)
+  // the four waves splitting K over all four 16-column tiles, for twice the
+  // workgroups: 16.7 -> 13.2 us. (With long K, split-K stays ahead: EP128
+  // gate_up at 64 columns and split 2 ran 21.6 us against 23.0 at 128 and
+  // split 4.)
   if (split == 1 && tiles < qma::kNumCUs && tm == 1 && wk == 1 && L.N % 64 == 0 &&
       L.k_chunks >= qma::kStreamChunks) {
     wk = 4;
@@ -150,8 +154,9 @@ void plan_small_m(const Layer& L, int32_t bm, int32_t tiles_m, qma_plan_t* p) {
     p->est_tiles = (int32_t)std::min<int64_t>((int64_t)tiles_m * (L.N / 64), 1 << 30);
   }
   p->split_k = split;
-  // the shared-row kernel (tm <= 2, one K partition, no split) keeps two
-  // chunks in flight per wave at three workgroups per CU
+  // the shared-row kernel keeps two chunks in flight per wave (its LDS ring
+  // and register stages); the per-wave-row kernel sizes its depth to its
+  // register budget
   const int depth = qma::small_m_shared_rows(tm, ntw, wk) ? 2 : qma::small_m_depth(tm, ntw);
   p->k_depth = depth * qma::kChunkK;
   // Short K (a down projection of a narrow TP share): a workgroup that saw
