@@ -417,7 +417,8 @@ def build_runner(name, seed, cache, schedule, overrides, fused=True):
     if schedule != "planner":
         applied = moe.set_schedule({"semi_static": qma.SCHEDULE_SEMI_STATIC,
                                     "dynamic": qma.SCHEDULE_DYNAMIC,
-                                    "gang": qma.SCHEDULE_GANG}[schedule])
+                                    "gang": qma.SCHEDULE_GANG,
+                                    "stream_k": qma.SCHEDULE_STREAM_K}[schedule])
     for which, ov in (("13", overrides.get("gate_up")), ("2", overrides.get("down"))):
         if ov:
             plan = getattr(moe, "plan" + which)
@@ -554,11 +555,12 @@ def main():
                     help="silu(gate) * up in gate_up's epilogue (fused, the default) or as its "
                          "own kernel between the GEMMs (separate)")
     ap.add_argument("--schedule", default="planner",
-                    choices=("planner", "semi_static", "dynamic", "gang"),
+                    choices=("planner", "semi_static", "dynamic", "gang", "stream_k"),
                     help="how small-M GEMMs hand out (tile, column block) work: the "
                          "planner's choice, or one schedule forced where the plan accepts "
                          "it (dynamic: 16/32-row tiles, one K partition; gang: the "
-                         "shared-row instances)")
+                         "shared-row instances; stream_k: their 16/32-row indexed plans "
+                         "without split-K)")
     ap.add_argument("--override-gate-up", default="",
                     help="JSON object of plan fields to set on the headline workload's "
                          "gate_up plan before timing (A/B runs, e.g. '{\"split_k\": 1}')")

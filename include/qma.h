@@ -174,11 +174,26 @@ typedef struct qma_plan {
  *     width, then 256, then 128 columns. Accepted for waves_k = 1,
  *     n_stream = 1, block_n 128 or 256 and block_m 16, 32 or 64 (the
  *     shared-row instances), with or without split-K; other plans ->
- *     QMA_ERR_INVALID_ARG. No workspace beyond split-K's. */
+ *     QMA_ERR_INVALID_ARG. No workspace beyond split-K's.
+ *   STREAM_K: the gang's one workgroup per CU, for launches of several
+ *     rounds. Each CU takes a contiguous share of the (token tile, column
+ *     block) items, balanced to one item, and its groups split the share's
+ *     K chunks evenly, so an item may be cut in K between neighbouring
+ *     groups of a CU ([release] indexed techniques: stream-K). The pieces
+ *     meet in LDS and are added in K order, so the result is that of
+ *     split-K over the same cut points: with integer-exact inputs, bit for
+ *     bit the unsplit result. Accepted on the INDEXED path for waves_k = 1, n_stream = 1,
+ *     split_k = 1, block_m 16 or 32, block_n 128 or 256 and at least 8 K
+ *     chunks; other plans -> QMA_ERR_INVALID_ARG. A call whose sorted
+ *     capacity could give one group items of three token tiles (column
+ *     blocks per tile fewer than the items per group) -> QMA_ERR_INVALID_ARG.
+ *     No workspace. The planner does not pick it: on the measured shapes
+ *     the gang and semi-static schedules were as fast or faster. */
 typedef enum {
   QMA_SCHEDULE_SEMI_STATIC = 0,
   QMA_SCHEDULE_DYNAMIC = 1,
-  QMA_SCHEDULE_GANG = 2
+  QMA_SCHEDULE_GANG = 2,
+  QMA_SCHEDULE_STREAM_K = 3
 } qma_schedule;
 
 /* ---- layer (load time) ------------------------------------------------ */

@@ -288,8 +288,11 @@ qma_status check_layer_plan(const qma_layer_t* layer, const qma_plan_t* plan,
       plan->kernel == QMA_KERNEL_SMALL_M && plan->waves_k == 1 && plan->n_stream == 1 &&
       (plan->block_n == 128 || plan->block_n == 256) && plan->block_m % 16 == 0 &&
       qma::small_m_shared_rows(plan->block_m / 16, plan->block_n / 64, 1);
+  const bool stream_k_ok = gang_ok && L.path == QMA_PATH_INDEXED && plan->split_k == 1 &&
+                           plan->block_m <= 32 && L.k_chunks >= qma::kStreamChunks;
   if (plan->schedule != QMA_SCHEDULE_SEMI_STATIC &&
       !(plan->schedule == QMA_SCHEDULE_GANG && gang_ok) &&
+      !(plan->schedule == QMA_SCHEDULE_STREAM_K && stream_k_ok) &&
       (plan->schedule != QMA_SCHEDULE_DYNAMIC || plan->kernel != QMA_KERNEL_SMALL_M ||
        plan->waves_k != 1 || plan->split_k != 1 || plan->n_stream != 1 ||
        (plan->block_m != 16 && plan->block_m != 32) ||
@@ -684,6 +687,13 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
   if ((s = check_a_bytes(a_rows, layer->L.K)) != QMA_OK) return s;
   if ((s = check_grid(((int64_t)sorted_cap + plan->block_m - 1) / plan->block_m, plan)) != QMA_OK)
     return s;
+  if (plan->schedule == QMA_SCHEDULE_STREAM_K &&
+      !qma::stream_k_fits(((int64_t)sorted_cap + plan->block_m - 1) / plan->block_m,
+                          layer->L.N / plan->block_n, layer->L.k_chunks, plan->block_m / 16,
+                          plan->block_n / 64))
+    return fail(QMA_ERR_INVALID_ARG,
+                "stream-K: sorted_cap %d gives a group items of more than two token tiles "
+                "(%d column blocks per tile)", sorted_cap, layer->L.N / plan->block_n);
   if (num_slots == 0) return ok();
   qma::GemmArgs g{};
   g.layer = &layer->L;

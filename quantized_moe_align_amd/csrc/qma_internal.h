@@ -125,6 +125,24 @@ int launch_prepack(const Layer& L, const int32_t* qweight,
 int launch_silu_and_mul(const uint16_t* x, uint16_t* y, int64_t R, int32_t I,
                         void* stream);
 int launch_gemm(const GemmArgs& g, void* stream);
+
+// Groups per stream-K workgroup: four for the 128-column instances (at
+// most 128 VGPRs), three for the 256-column ones (at most 168).
+constexpr int sk_groups(int tm, int ntw) { return ntw == 4 ? 3 : 4; }
+
+// Whether a stream-K launch keeps every group's unit range within two token
+// tiles for any routed tile count up to num_tiles: a workgroup holds at
+// most ceil(items / CUs) items, a group ceil(that * KC / S) units, and a
+// range of L units touches at most 1 + ceil((L - 1) / KC) items.
+inline bool stream_k_fits(int64_t num_tiles, int64_t nblocks, int64_t kc, int tm, int ntw) {
+  const int S = sk_groups(tm, ntw);
+  if (num_tiles <= 0 || nblocks <= 0 || kc <= 0) return false;
+  const int64_t per_wg = (num_tiles * nblocks + kNumCUs - 1) / kNumCUs;
+  if (per_wg * kc >= (1ll << 30)) return false;
+  const int64_t per_group = (per_wg * kc + S - 1) / S;
+  const int64_t span = 1 + (per_group - 1 + kc - 1) / kc;
+  return span - 1 <= nblocks;
+}
 int launch_router_topk(const float* logits, int32_t T, int32_t E, int32_t topk,
                        int32_t* ids, float* w, void* stream);
 int launch_combine(const uint16_t* c2, const float* w, const int32_t* ids,

@@ -1056,6 +1056,133 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 template <int TM, int D>
 constexpr int xs_lds_bytes() { return D * TM * 16 * 256 + TM * 16 * 8; }
 
+template <int NTW>
+struct XsStage {
+  u32x4 w[NTW];
+  u32x2 s[NTW];
+};
+
+// One 128-wide K chunk of the shared-row kernels. The chunk's token rows
+// sit in LDS at xb (row r of tile tm at xb + (tm * 16 + r) * 256, segment
+// j of a row in slot j ^ (r % 16)), the wave's weight words and scales in
+// st; the products accumulate into acc (lane l: rows 4 * (l / 16) + i of
+// column l % 16 of each 16 x 16 tile).
+template <int TM, int NTW>
+__device__ __forceinline__ void xs_compute(f32x4 (&acc)[NTW][TM], const XsStage<NTW>& st,
+                                           uint32_t xb, int kb, int col) {
+  constexpr int XROW = 256;
+  const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+  // Four token tiles share each weight word: dequantising it once to
+  // bf16((q - 8) s) (about 19 VALU) then costs less than the exact form's
+  // per-tile scale FMAs (4 per tile) and zero-point MFMAs, and the MFMAs
+  // accumulate straight into acc. Fewer tiles keep the exact form.
+  constexpr bool kScaledW = TM >= 4;
+  if constexpr (TM == 1 && NTW == 4) {
+    // One token tile, four column tiles: the chunk's four fragments are
+    // read at once and their four zero-point MFMAs go first, so no
+    // product waits on the one just before it; products and scale FMAs
+    // then run pipelined by one over the chunk's (group, column tile)
+    // pairs. Same operations per accumulator, in the same order, as the
+    // general form below. (EP8 decode gate_up 132.6-133.1 -> 130.3-130.6
+    // us; with two column tiles the TP8 gate_up share ran 2.6 % slower
+    // than the general form, so that instance keeps it.)
+    u32x4 xg[4];
+    static_for<4>([&](auto g) { xg[g] = lds_read16<0>(xb + (((4 * g + kb) ^ col) << 4)); });
+    static_for<4>([&](auto g) { wait_lgkm<3 - g>(xg[g]); });
+    f32x4 xsum[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) xsum[g] = mfma16(xg[g], neg136, zero4);
+    f32x4 pr[2];
+    float scv[2];
+    auto product = [&](int i) {
+      const int g = i / NTW, nt = i % NTW;
+      const u32x4 wb = unpack_128q(st.w[nt][g]);
+      const uint32_t sw = st.s[nt][g >> 1];
+      scv[i & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+      pr[i & 1] = mfma16(xg[g], wb, xsum[g]);
+    };
+    auto scale = [&](int i) {
+      const int nt = i % NTW;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        acc[nt][0][r] = __builtin_fmaf(scv[i & 1], pr[i & 1][r], acc[nt][0][r]);
+    };
+    product(0);
+#pragma unroll
+    for (int i = 1; i < 4 * NTW; ++i) {
+      product(i);
+      scale(i - 1);
+    }
+    scale(4 * NTW - 1);
+    return;
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    const uint32_t a = xb + (((4 * g + kb) ^ col) << 4);
+    u32x4 xg[TM];
+    static_for<TM>([&](auto tm) { xg[tm] = lds_read16<tm * 16 * XROW>(a); });
+    static_for<TM>([&](auto tm) { wait_lgkm<TM - 1 - tm>(xg[tm]); });
+    if constexpr (kScaledW) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const uint32_t sw = st.s[nt][g >> 1];
+        const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+        const u32x4 wb = dequant8(st.w[nt][g], scv, -8.0f * scv);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = mfma16(xg[tm], wb, acc[nt][tm]);
+      }
+      continue;
+    }
+    f32x4 xsum[TM];
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) xsum[tm] = mfma16(xg[tm], neg136, zero4);
+    // Pipelined by one column tile: tile nt's products are issued before
+    // tile nt-1's scale FMAs, so the FMAs run while the matrix core works
+    // instead of waiting out each product's latency. Every accumulator
+    // takes the same operations in the same order as the plain loop
+    // (kept for reference and for instances that would not fit).
+    if constexpr (TM * NTW > 8) {
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt) {
+        const u32x4 wb = unpack_128q(st.w[nt][g]);
+        const uint32_t sw = st.s[nt][g >> 1];
+        const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+#pragma unroll
+        for (int tm = 0; tm < TM; ++tm) {
+          const f32x4 p1 = mfma16(xg[tm], wb, xsum[tm]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) acc[nt][tm][r] = __builtin_fmaf(sc, p1[r], acc[nt][tm][r]);
+        }
+      }
+      continue;
+    }
+    f32x4 pr[2][TM];
+    float scv[2];
+    auto product = [&](int nt) {
+      const u32x4 wb = unpack_128q(st.w[nt][g]);
+      const uint32_t sw = st.s[nt][g >> 1];
+      scv[nt & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) pr[nt & 1][tm] = mfma16(xg[tm], wb, xsum[tm]);
+    };
+    auto scale = [&](int nt) {
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          acc[nt][tm][r] = __builtin_fmaf(scv[nt & 1], pr[nt & 1][tm][r], acc[nt][tm][r]);
+    };
+    product(0);
+#pragma unroll
+    for (int nt = 1; nt < NTW; ++nt) {
+      product(nt);
+      scale(nt - 1);
+    }
+    scale(NTW - 1);
+  }
+}
+
 // One (token tile, column block, K split) of the shared-row kernel; s_x
 // holds xs_lds_bytes<TM, D>() bytes of LDS: the D token buffers, then the
 // tile's output rows and topk weights (TM * 16 of each).
@@ -1119,11 +1246,7 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   // step f -> K chunk; past the end the last chunk is fetched again, so
   // every step issues the same loads
   auto chunk = [&](int f) { return cs0 + min(f, total - 1); };
-  struct WStage {
-    u32x4 w[NTW];
-    u32x2 s[NTW];
-  };
-  auto load_w = [&](WStage& st, int f) {
+  auto load_w = [&](XsStage<NTW>& st, int f) {
     const int c = chunk(f);
 #pragma unroll
     for (int nt = 0; nt < NTW; ++nt)
@@ -1151,121 +1274,12 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   for (int nt = 0; nt < NTW; ++nt)
 #pragma unroll
     for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x4 neg136 = {0xC308C308u, 0xC308C308u, 0xC308C308u, 0xC308C308u};
-  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
   // operand read: row tm*16 + l%16, segment 4g + l/16 at slot segment ^ (l%16)
   const uint32_t xrd = lds_addr(s_x) + col * XROW;
 
-  // Four token tiles share each weight word: dequantising it once to
-  // bf16((q - 8) s) (about 19 VALU) then costs less than the exact form's
-  // per-tile scale FMAs (4 per tile) and zero-point MFMAs, and the MFMAs
-  // accumulate straight into acc. Fewer tiles keep the exact form.
-  constexpr bool kScaledW = TM >= 4;
-  auto compute = [&](auto buf_id, const WStage& st) {
+  auto compute = [&](auto buf_id, const XsStage<NTW>& st) {
     constexpr int b = decltype(buf_id)::value;
-    if constexpr (TM == 1 && NTW == 4) {
-      // One token tile, four column tiles: the chunk's four fragments are
-      // read at once and their four zero-point MFMAs go first, so no
-      // product waits on the one just before it; products and scale FMAs
-      // then run pipelined by one over the chunk's (group, column tile)
-      // pairs. Same operations per accumulator, in the same order, as the
-      // general form below. (EP8 decode gate_up 132.6-133.1 -> 130.3-130.6
-      // us; with two column tiles the TP8 gate_up share ran 2.6 % slower
-      // than the general form, so that instance keeps it.)
-      u32x4 xg[4];
-      static_for<4>([&](auto g) { xg[g] = lds_read16<0>(xrd + b * XBUF + (((4 * g + kb) ^ col) << 4)); });
-      static_for<4>([&](auto g) { wait_lgkm<3 - g>(xg[g]); });
-      f32x4 xsum[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g) xsum[g] = mfma16(xg[g], neg136, zero4);
-      f32x4 pr[2];
-      float scv[2];
-      auto product = [&](int i) {
-        const int g = i / NTW, nt = i % NTW;
-        const u32x4 wb = unpack_128q(st.w[nt][g]);
-        const uint32_t sw = st.s[nt][g >> 1];
-        scv[i & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        pr[i & 1] = mfma16(xg[g], wb, xsum[g]);
-      };
-      auto scale = [&](int i) {
-        const int nt = i % NTW;
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          acc[nt][0][r] = __builtin_fmaf(scv[i & 1], pr[i & 1][r], acc[nt][0][r]);
-      };
-      product(0);
-#pragma unroll
-      for (int i = 1; i < 4 * NTW; ++i) {
-        product(i);
-        scale(i - 1);
-      }
-      scale(4 * NTW - 1);
-      return;
-    }
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const uint32_t a = xrd + b * XBUF + (((4 * g + kb) ^ col) << 4);
-      u32x4 xg[TM];
-      static_for<TM>([&](auto tm) { xg[tm] = lds_read16<tm * 16 * XROW>(a); });
-      static_for<TM>([&](auto tm) { wait_lgkm<TM - 1 - tm>(xg[tm]); });
-      if constexpr (kScaledW) {
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const uint32_t sw = st.s[nt][g >> 1];
-          const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-          const u32x4 wb = dequant8(st.w[nt][g], scv, -8.0f * scv);
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = mfma16(xg[tm], wb, acc[nt][tm]);
-        }
-        continue;
-      }
-      f32x4 xsum[TM];
-#pragma unroll
-      for (int tm = 0; tm < TM; ++tm) xsum[tm] = mfma16(xg[tm], neg136, zero4);
-      // Pipelined by one column tile: tile nt's products are issued before
-      // tile nt-1's scale FMAs, so the FMAs run while the matrix core works
-      // instead of waiting out each product's latency. Every accumulator
-      // takes the same operations in the same order as the plain loop
-      // (kept for reference and for instances that would not fit).
-      if constexpr (TM * NTW > 8) {
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) {
-          const u32x4 wb = unpack_128q(st.w[nt][g]);
-          const uint32_t sw = st.s[nt][g >> 1];
-          const float sc = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-#pragma unroll
-          for (int tm = 0; tm < TM; ++tm) {
-            const f32x4 p1 = mfma16(xg[tm], wb, xsum[tm]);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) acc[nt][tm][r] = __builtin_fmaf(sc, p1[r], acc[nt][tm][r]);
-          }
-        }
-        continue;
-      }
-      f32x4 pr[2][TM];
-      float scv[2];
-      auto product = [&](int nt) {
-        const u32x4 wb = unpack_128q(st.w[nt][g]);
-        const uint32_t sw = st.s[nt][g >> 1];
-        scv[nt & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm) pr[nt & 1][tm] = mfma16(xg[tm], wb, xsum[tm]);
-      };
-      auto scale = [&](int nt) {
-#pragma unroll
-        for (int tm = 0; tm < TM; ++tm)
-#pragma unroll
-          for (int r = 0; r < 4; ++r)
-            acc[nt][tm][r] = __builtin_fmaf(scv[nt & 1], pr[nt & 1][tm][r], acc[nt][tm][r]);
-      };
-      product(0);
-#pragma unroll
-      for (int nt = 1; nt < NTW; ++nt) {
-        product(nt);
-        scale(nt - 1);
-      }
-      scale(NTW - 1);
-    }
+    xs_compute<TM, NTW>(acc, st, xrd + b * XBUF, kb, col);
   };
 
   // Pipeline. Issue order: prologue W(0) X(0) W(1) X(1) .. X(D-2) W(D-1);
@@ -1273,7 +1287,7 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   // chunk j, W(j+D). When step j waits, the loads issued after X(j) are
   // W(j+1) and D-2 pairs (X, W): that count is exact on every step.
   constexpr int kAfter = NW + (D - 2) * (NX + NW);
-  WStage ws[D];
+  XsStage<NTW> ws[D];
   static_for<D - 1>([&](auto d) {
     load_w(ws[d], d);
     load_x(d, d);
@@ -1294,16 +1308,16 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
     __builtin_amdgcn_sched_barrier(0);
     load_w(ws[b], j + D);
   };
-  for (int j = 0;; j += D) {
-    bool done = false;
-    static_for<D>([&](auto d) {
-      if (!done) {
-        step(j + d, d);
-        if (j + d + 1 >= total) done = true;
-      }
-    });
-    if (done) break;
-  }
+  // Whole rounds of D steps, then the last total % D. Every step of the
+  // loop body runs unconditionally: a step that could be skipped inside the
+  // loop would let the compiler assume a path on which the next step's
+  // weights have fewer loads behind them, and it would then wait for the
+  // stage issued one step ahead before computing.
+  int j = 0;
+  for (; j + D <= total; j += D) static_for<D>([&](auto d) { step(j + d, d); });
+  static_for<D - 1>([&](auto d) {
+    if (j + d < total) step(j + d, d);
+  });
   wait_vmcnt<0>();
   // every wave's view of the row table (a one-chunk range has had no
   // barrier since wave 0 wrote it)
@@ -1411,6 +1425,306 @@ __global__ __launch_bounds__(256 * S, 1) void gemm_small_m_xs_gang_kernel(const 
     // the group's LDS ring and row table are free for its next item
     __syncthreads();
   }
+}
+
+// Stream-K gang schedule: one workgroup of S four-wave groups per CU, each
+// CU taking a contiguous share of the (token tile, column block) items,
+// balanced to one item over the CUs. Inside the workgroup the share's K
+// chunks are split evenly over the groups, so an item can be cut in K
+// between neighbouring groups; the groups advance in lock-step through
+// the per-chunk barrier and end together, and no CU idles at the end of
+// the launch as a semi-static grid's last round leaves it. A group walks
+// its chunks as one stream through the shared-row pipeline: the next
+// item's loads are in flight while the current one finishes. A finished
+// item is packed to bf16 at once and stored at the next step, ahead of
+// that step's loads, so the pipeline's wait counts never include stores.
+// An item cut in K: the group holding its first chunk (the owner) keeps
+// its piece in registers to the end; a group whose range starts inside
+// the item leaves its piece as fp32 in its LDS slot, and after the final
+// barrier the owner adds the later pieces in K order (the ordered split
+// reduction of split-K, inside one workgroup). Items are ordered token
+// tile by column block, and the CU shares of one XCD are contiguous, so a
+// tile's token rows stay in few L2s. Indexed (moe_align) routing only;
+// the host keeps every group's range within two token tiles.
+template <int TM, int NTW>
+constexpr int sk_group_bytes() {
+  return (2 * TM * 16 * 256 + 2 * TM * 16 * 8 + TM * 16 * 64 * NTW * 4 + 1023) / 1024 * 1024;
+}
+
+__device__ __forceinline__ void lds_write16(uint32_t addr, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(addr), "v"(v) : "memory");
+}
+
+// The body of the stream-K kernel; lds holds S * sk_group_bytes<TM, NTW>()
+// bytes: per group its token ring, the row tables of two tiles and its slot.
+template <int TM, int NTW, int S>
+__device__ __forceinline__ void sk_workgroup(const GemmParams& p, uint8_t* lds) {
+  constexpr int D = 2;
+  constexpr int XROW = 256;
+  constexpr int XBUF = TM * 16 * XROW;
+  constexpr int NX = TM;
+  constexpr int NW = 2 * NTW;
+  constexpr int ROWS = TM * 16;
+  constexpr int GB = sk_group_bytes<TM, NTW>();
+  static_assert(2 * ROWS <= 64 && NTW % 2 == 0, "row tables of two tiles come from one wave");
+  const int g = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
+  const int tid = (int)(threadIdx.x & 255);
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 15, kb = lane >> 4;
+  uint8_t* s_x = lds + g * GB;
+  int32_t* s_orow = (int32_t*)(s_x + D * XBUF);  // [2][ROWS]: output rows of the two tiles
+  float* s_tw = (float*)(s_orow + 2 * ROWS);     // [2][ROWS]: their topk weights
+  // fp32 piece of group k in lane layout: f32x4 (w, tm, nt) at lane * 16
+  auto slot_addr = [&](int k, int tm, int nt) __attribute__((always_inline)) {
+    return lds_addr(lds) + (uint32_t)(k * GB + D * XBUF + 2 * ROWS * 8 +
+                                      ((w * TM + tm) * NTW + nt) * 1024 + lane * 16);
+  };
+
+  // This workgroup's items [i0, i1) and this group's units (K chunks,
+  // counted from item i0's first chunk) [ua, ub).
+  const int KC = p.KC, nbl = p.nblocks;
+  const int ntiles = min(*p.ntp / p.BM, p.num_tiles);
+  const int64_t items = (int64_t)max(ntiles, 0) * nbl;
+  const int grid = (int)gridDim.x;
+  const int rk = (int)(blockIdx.x & 7) * (grid >> 3) + (int)(blockIdx.x >> 3);
+  const int64_t i0 = items * rk / grid, i1 = items * (rk + 1) / grid;
+  if (i0 >= i1) return;
+  const int64_t U = (i1 - i0) * KC;
+  auto ustart = [&](int k) __attribute__((always_inline)) { return (int)(U * k / S); };
+  const int ua = ustart(g), ub = ustart(g + 1);
+  const int n = ub - ua;                    // >= 2: U >= KC >= 8 > S
+  const int nmax = (int)((U + S - 1) / S);  // steps of the longest group
+  const int64_t ia = i0 + ua / KC, ib = i0 + (ub - 1) / KC;
+  const int tA = (int)(ia / nbl), tB = (int)(ib / nbl);
+  const int eA = __builtin_amdgcn_readfirstlane(tile_expert(p, tA));
+  const int eB = __builtin_amdgcn_readfirstlane(tile_expert(p, tB));
+
+  // weights and scales of the two tiles' experts (none for a tile whose
+  // expert id is out of range: its items then read zeros and store nothing)
+  const uint32_t wbytes = (uint32_t)p.NT * KC * kWBlockBytes;
+  const uint32_t sbytes = (uint32_t)p.NT * KC * kSBlockBytes;
+  const __amdgpu_buffer_rsrc_t rwA = make_rsrc(p.wpk + (size_t)max(eA, 0) * wbytes, eA >= 0 ? wbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rwB = make_rsrc(p.wpk + (size_t)max(eB, 0) * wbytes, eB >= 0 ? wbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rsA = make_rsrc(p.spk + (size_t)max(eA, 0) * sbytes, eA >= 0 ? sbytes : 0u);
+  const __amdgpu_buffer_rsrc_t rsB = make_rsrc(p.spk + (size_t)max(eB, 0) * sbytes, eB >= 0 ? sbytes : 0u);
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a, p.a_bytes);
+  const uint32_t voff_w = lane * 16, voff_s = col * 8;
+  // token rows: wave w copies rows 4 (w * NX + i) + l / 16 of the tile
+  uint32_t vxA[NX], vxB[NX];
+#pragma unroll
+  for (int i = 0; i < NX; ++i) {
+    const int row = 4 * (w * NX + i) + kb;
+    const uint32_t seg = (uint32_t)(col ^ (row & 15));
+    const RowInfo r0 = row_info(p, tA, eA, row), r1 = row_info(p, tB, eB, row);
+    vxA[i] = (r0.valid && eA >= 0) ? (uint32_t)r0.a_row * (uint32_t)p.K * 2u + seg * 16u
+                                   : 0x80000000u;
+    vxB[i] = (r1.valid && eB >= 0) ? (uint32_t)r1.a_row * (uint32_t)p.K * 2u + seg * 16u
+                                   : 0x80000000u;
+  }
+  // output rows and topk weights of both tiles: wave 0 looks them up here
+  // and parks them in LDS after the prologue
+  int32_t my_orow = -1;
+  float my_tw = 1.0f;
+  if (w == 0 && lane < 2 * ROWS) {
+    const bool second = lane >= ROWS;
+    const int t = second ? tB : tA, e = second ? eB : eA;
+    const RowInfo ri = row_info(p, t, e, lane - (second ? ROWS : 0));
+    my_orow = (ri.valid && e >= 0) ? ri.out_row : -1;
+    my_tw = (ri.valid && e >= 0 && p.mode == 0 && p.topk_w) ? p.topk_w[ri.out_row] : 1.0f;
+  }
+
+  // Cursor over the group's units: K chunk, column block and token tile
+  // (0: tA, 1: tB) of the next unit to load or compute. It stays on the
+  // last unit once there, so loads past the end fetch that unit again.
+  struct Cursor {
+    int c, nb, t, left;
+  };
+  auto advance = [&](Cursor& q) __attribute__((always_inline)) {
+    if (q.left > 1) {
+      --q.left;
+      if (++q.c == KC) {
+        q.c = 0;
+        if (++q.nb == nbl) {
+          q.nb = 0;
+          q.t = 1;
+        }
+      }
+    }
+  };
+  const Cursor c0{ua % KC, (int)(ia % nbl), 0, n};
+  Cursor wcur = c0, xcur = c0, ccur = c0;
+
+  auto load_w = [&](XsStage<NTW>& st) __attribute__((always_inline)) {
+    const int t0 = (wcur.nb * 4 + w) * NTW;
+    const TileAddr wa = tile_addr(p, t0, kWBlockBytes), sa = tile_addr(p, t0, kSBlockBytes);
+    const __amdgpu_buffer_rsrc_t rw = wcur.t ? rwB : rwA;
+    const __amdgpu_buffer_rsrc_t rs = wcur.t ? rsB : rsA;
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      st.w[nt] = __builtin_amdgcn_raw_buffer_load_b128(
+          rw, voff_w, wa.base + nt * wa.tile + wcur.c * wa.chunk, kNonTemporal);
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+      st.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(
+          rs, voff_s, sa.base + nt * sa.tile + wcur.c * sa.chunk, 0);
+    advance(wcur);
+  };
+  auto load_x = [&](auto buf_id) __attribute__((always_inline)) {
+    constexpr int b = decltype(buf_id)::value;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const uint32_t vo = xcur.t ? vxB[i] : vxA[i];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          ra,
+          (__attribute__((address_space(3))) void*)(s_x + b * XBUF + 4 * (w * NX + i) * XROW),
+          16, (int)vo, xcur.c * XROW, 0, 0);
+    }
+    advance(xcur);
+  };
+
+  f32x4 acc[NTW][TM];
+  auto zero_acc = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int nt = 0; nt < NTW; ++nt)
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm) acc[nt][tm] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  zero_acc();
+  const uint32_t xrd = lds_addr(s_x) + col * XROW;
+  const uint32_t tbl = lds_addr(s_orow) + kb * 16;
+
+  // Store the finished item in acc: rows 4 kb + r of column col of each
+  // tile, scaled by the rows' topk weights and rounded to bf16 (with the
+  // activation fused: output tile q from gate tile 2 q and up tile 2 q + 1).
+  auto store_item = [&](int t, int nb) __attribute__((always_inline)) {
+    const int t0 = (nb * 4 + w) * NTW;
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm) {
+      // LDS reads the compiler does not track (it would wait for every
+      // direct-to-LDS load in flight before its own)
+      u32x4 rv = lds_read16<0>(tbl + (uint32_t)((t * ROWS + tm * 16) * 4));
+      u32x4 tv = lds_read16<0>(tbl + (uint32_t)((2 * ROWS + t * ROWS + tm * 16) * 4));
+      wait_lgkm<0>(rv);
+      wait_lgkm<0>(tv);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int orow = (int)rv[r];
+        const float twr = __uint_as_float(tv[r]);
+        if (orow < 0) continue;
+        if (p.act) {
+#pragma unroll
+          for (int q = 0; q < NTW / 2; ++q)
+            p.c[(size_t)orow * (p.N / 2) + (t0 / 2 + q) * 16 + col] =
+                fused_silu_mul(acc[2 * q][tm][r] * twr, acc[2 * q + 1][tm][r] * twr);
+        } else {
+#pragma unroll
+          for (int nt = 0; nt < NTW; ++nt)
+            p.c[(size_t)orow * p.N + (t0 + nt) * 16 + col] =
+                (uint16_t)(pack_bf16x2(acc[nt][tm][r] * twr, 0.f) & 0xFFFFu);
+        }
+      }
+    }
+  };
+  auto put_slot = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+      for (int nt = 0; nt < NTW; ++nt)
+        lds_write16(slot_addr(g, tm, nt), __builtin_bit_cast(u32x4, acc[nt][tm]));
+  };
+
+  // Pipeline (as the shared-row kernel, D = 2): prologue W(0) X(0) W(1);
+  // step j: [wait, barrier] the store of an item finished at step j - 1
+  // (still in acc), X(j+1) into the buffer of chunk j - 1, chunk j,
+  // W(j+2). When step j waits, only W(j+1) was issued after X(j): stores
+  // go out ahead of the step's loads, so the count holds.
+  XsStage<NTW> ws[D];
+  load_w(ws[0]);
+  load_x(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_sched_barrier(0);
+  load_w(ws[1]);
+  if (w == 0 && lane < 2 * ROWS) {
+    s_orow[lane] = my_orow;
+    s_tw[lane] = my_tw;
+    // written before the first (bare) barrier lets other waves read them
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  }
+  bool from0 = c0.c == 0;  // the piece in acc began at its item's first chunk
+  bool pend = false;
+  int pend_t = 0, pend_nb = 0;
+  auto step = [&](int j, auto cur) __attribute__((always_inline)) {
+    constexpr int b = decltype(cur)::value;
+    wait_vmcnt<NW>();
+    lds_barrier();
+    if (pend) {
+      store_item(pend_t, pend_nb);
+      zero_acc();
+      pend = false;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(std::integral_constant<int, b ^ 1>{});
+    __builtin_amdgcn_sched_barrier(0);
+    if (j < n) {
+      xs_compute<TM, NTW>(acc, ws[b], xrd + b * XBUF, kb, col);
+      if (j < n - 1 && ccur.c == KC - 1) {
+        // an item's last chunk: a whole item stays in acc for the store at
+        // the next step; a piece that began inside the item goes to the
+        // slot for its owner
+        if (from0) {
+          pend = true;
+          pend_t = ccur.t;
+          pend_nb = ccur.nb;
+        } else {
+          put_slot();
+          zero_acc();
+        }
+        from0 = true;
+      }
+      advance(ccur);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_w(ws[b]);
+  };
+  // both steps of the loop body unconditional (see the shared-row kernel)
+  int j = 0;
+  for (; j + 2 <= nmax; j += 2) {
+    step(j, std::integral_constant<int, 0>{});
+    step(j + 1, std::integral_constant<int, 1>{});
+  }
+  if (j < nmax) step(j, std::integral_constant<int, 0>{});
+  wait_vmcnt<0>();
+  // The last piece: a whole item is stored; a piece that began inside its
+  // item goes to the slot; the owner of an item that continues in the next
+  // groups adds their pieces (each began inside the item) in K order.
+  if (!from0) put_slot();
+  // the slot writes are inline asm, which the barrier's own wait may not
+  // count
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+  if (!from0) return;
+  if (ccur.c != KC - 1) {
+    const int xe = ((ub - 1) / KC + 1) * KC;  // end of the item, in units
+    for (int k = g + 1; k < S; ++k) {
+      if (ustart(k) >= xe) break;
+#pragma unroll
+      for (int tm = 0; tm < TM; ++tm)
+#pragma unroll
+        for (int nt = 0; nt < NTW; ++nt) {
+          u32x4 v = lds_read16<0>(slot_addr(k, tm, nt));
+          wait_lgkm<0>(v);
+          acc[nt][tm] += __builtin_bit_cast(f32x4, v);
+        }
+      if (ustart(k + 1) >= xe) break;
+    }
+  }
+  store_item(ccur.t, ccur.nb);
+}
+
+template <int TM, int NTW, int S>
+__global__ __launch_bounds__(256 * S, 1) void gemm_small_m_sk_kernel(const GemmParams p) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[S * sk_group_bytes<TM, NTW>()];
+  sk_workgroup<TM, NTW, S>(p, lds);
 }
 
 __global__ void reset_counter_kernel(int32_t* c) {
@@ -2379,6 +2693,20 @@ static int launch_xs_gang(const GemmParams& gp, int64_t items, hipStream_t st) {
   return (int)hipGetLastError();
 }
 
+// Stream-K gang: one workgroup per CU (the launch asks for more than half a
+// CU's LDS), S groups of four waves. The kernel keeps a group's items
+// within two token tiles; the caller checks that bound for the call.
+template <int TM, int NTW, int S>
+static int launch_sk(const GemmParams& gp, hipStream_t st) {
+  constexpr size_t stat = (size_t)S * sk_group_bytes<TM, NTW>();
+  static_assert(stat <= (size_t)kLdsPerCU, "stream-K groups exceed a CU's LDS");
+  constexpr size_t one_per_cu = kLdsPerCU / 2 + 1024;
+  const size_t dyn = stat < one_per_cu ? one_per_cu - stat : 0;
+  hipLaunchKernelGGL((gemm_small_m_sk_kernel<TM, NTW, S>), dim3((unsigned)kNumCUs),
+                     dim3(256 * S), dyn, st, gp);
+  return (int)hipGetLastError();
+}
+
 // Token tiles the plan expects (its estimate, est_tiles / column blocks).
 static int64_t plan_tiles_m(const qma_plan_t& pl) {
   const int64_t nb = pl.block_n > 0 ? pl.n / pl.block_n : 0;
@@ -2483,7 +2811,20 @@ int launch_gemm(const GemmArgs& g, void* stream) {
     gp.fold = xcd_fold(plan_tiles_m(pl), gp.nblocks);
     const int64_t vt_pad = ((int64_t)g.num_tiles * gp.fold + 7) / 8 * 8;
     const dim3 sg((unsigned)(vt_pad * (gp.nblocks / gp.fold) * gp.split));
-    if (pl.schedule == QMA_SCHEDULE_GANG) {
+    if (pl.schedule == QMA_SCHEDULE_STREAM_K) {
+      if (!xs || g.mode != 0 || gp.split != 1 || tm > 2 || gp.KC < kStreamChunks ||
+          gp.nstream != 1 || !stream_k_fits(g.num_tiles, gp.nblocks, gp.KC, tm, ntw))
+        return (int)hipErrorInvalidConfiguration;
+      gp.fold = 1;
+      if (tm == 1 && ntw == 4)
+        err = launch_sk<1, 4, sk_groups(1, 4)>(gp, st);
+      else if (tm == 1)
+        err = launch_sk<1, 2, sk_groups(1, 2)>(gp, st);
+      else if (ntw == 4)
+        err = launch_sk<2, 4, sk_groups(2, 4)>(gp, st);
+      else
+        err = launch_sk<2, 2, sk_groups(2, 2)>(gp, st);
+    } else if (pl.schedule == QMA_SCHEDULE_GANG) {
       if (!xs) return (int)hipErrorInvalidConfiguration;
       if (tm == 1 && ntw == 4)
         err = launch_xs_gang<1, 4>(gp, sg.x, st);

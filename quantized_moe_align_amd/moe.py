@@ -87,7 +87,9 @@ def schedule_applies(plan: qma.Plan, schedule: int = qma.SCHEDULE_DYNAMIC) -> bo
     16/32-row small-M tiles with one K partition, no split-K and no
     column-block streaming; gang for the shared-row small-M instances (one K
     partition per workgroup, 128 or 256 columns, 16/32/64-row tiles, with
-    or without split-K, no streaming)."""
+    or without split-K, no streaming); stream-K for the 16/32-row shared-row
+    instances of an indexed layer without split-K (the call may still refuse
+    a sorted capacity that gives a group three token tiles)."""
     if schedule == qma.SCHEDULE_SEMI_STATIC:
         return True
     shared = (plan.kernel == qma.KERNEL_SMALL_M and plan.waves_k == 1 and plan.n_stream == 1
@@ -97,6 +99,9 @@ def schedule_applies(plan: qma.Plan, schedule: int = qma.SCHEDULE_DYNAMIC) -> bo
     if schedule == qma.SCHEDULE_GANG:
         return shared and (plan.block_m, plan.block_n) in ((16, 128), (16, 256), (32, 128),
                                                            (32, 256), (64, 128))
+    if schedule == qma.SCHEDULE_STREAM_K:
+        return (shared and plan.path == qma.PATH_INDEXED and plan.split_k == 1
+                and plan.block_m in (16, 32) and plan.k >= 8 * 128)
     return False
 
 

@@ -15,9 +15,9 @@ from typing import Optional
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libqma.so")
 
-SCHEDULE_SEMI_STATIC, SCHEDULE_DYNAMIC, SCHEDULE_GANG = 0, 1, 2
+SCHEDULE_SEMI_STATIC, SCHEDULE_DYNAMIC, SCHEDULE_GANG, SCHEDULE_STREAM_K = 0, 1, 2, 3
 LAYER_FUSE_SILU_MUL = 1
-SCHEDULE_NAMES = {0: "semi_static", 1: "dynamic", 2: "gang"}
+SCHEDULE_NAMES = {0: "semi_static", 1: "dynamic", 2: "gang", 3: "stream_k"}
 
 QMA_OK, QMA_ERR_INVALID_ARG, QMA_ERR_UNSUPPORTED, QMA_ERR_ROUTING, \
     QMA_ERR_WORKSPACE, QMA_ERR_HIP = range(6)

@@ -809,6 +809,81 @@ def test_gang_schedule_grouped(gpu):
         assert np.all(got_m[row_e < 0] == SENT)
 
 
+# Stream-K gang schedule (one workgroup per CU holding a contiguous share of
+# the items, its groups splitting the share's K chunks evenly, pieces of an
+# item cut in K added in LDS in K order): with integer-exact inputs every
+# partial sum is exact, so the output equals the semi-static grid's and the
+# oracle's bit for bit, and with the activation fused the activation kernel
+# on that output. The shapes give many items per CU with ragged expert
+# counts and slots routed off the rank, fewer items than CUs (items cut
+# over three or four groups), an EP8-down-like share, and a K of 9 chunks.
+SK_CASES = [  # (E, T, topk, K, N, block_m, block_n)
+    (37, 700, 2, 1024, 2048, 16, 128),
+    (37, 700, 2, 1024, 2048, 16, 256),
+    (37, 400, 2, 1024, 2048, 32, 128),
+    (37, 400, 2, 1024, 2048, 32, 256),
+    (5, 60, 2, 2048, 512, 16, 128),
+    (48, 280, 2, 2048, 7168, 16, 128),
+    (3, 9, 1, 1152, 256, 16, 128),
+]
+
+
+@pytest.mark.parametrize("case", SK_CASES)
+def test_stream_k_matches_semi_static(gpu, case):
+    E, T, topk, K, N, bm, bn = case
+    print(f"stream-K case {case}", flush=True)
+    rng = np.random.default_rng(400 + sum(case))
+    w, s = weights(rng, E, N, K, integer=True)
+    a = bf16_small_ints(rng, (T, K))
+    ids = rng.integers(-1, E, (T, topk)).astype(np.int32)
+    if E > 2:
+        ids[ids == 2] = 1                            # one expert with no rows
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": bm, "block_n": bn, "waves_k": 1,
+          "split_k": 1, "n_stream": 1}
+    static, _ = indexed(a, topk, ids, w, s, force_bm=bm, override=ov)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=bm, junk_tail=True,
+                        override=dict(ov, schedule=qma.SCHEDULE_STREAM_K))
+    assert plan.schedule == qma.SCHEDULE_STREAM_K
+    assert np.array_equal(got, static)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s)
+    valid = slot_experts(ids, E) >= 0
+    assert np.array_equal(got[valid], rne(ref[valid]))
+    assert np.all(got[~valid] == SENT)
+    h, _ = indexed(a, topk, ids, w, s, force_bm=bm, flags=qma.LAYER_FUSE_SILU_MUL,
+                   override=dict(ov, schedule=qma.SCHEDULE_STREAM_K))
+    h_ref = silu_of(static)
+    assert np.array_equal(h[valid], h_ref[valid])
+    assert np.all(h[~valid] == SENT)
+
+
+def test_stream_k_random_within_tolerance(gpu):
+    # random inputs: the cut points change only the fp32 summation order
+    E, T, topk, K, N = 24, 300, 2, 2048, 1536
+    rng = np.random.default_rng(420)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = rng.integers(0, E, (T, topk)).astype(np.int32)
+    tw = rng.random((T, topk)).astype(np.float32)
+    ov = {"kernel": qma.KERNEL_SMALL_M, "block_m": 16, "block_n": 128, "waves_k": 1,
+          "split_k": 1, "n_stream": 1, "schedule": qma.SCHEDULE_STREAM_K}
+    got, _ = indexed(a, topk, ids, w, s, force_bm=16, override=ov, topk_w=tw)
+    ref = O.moe_gemm_by_slot(a, topk, ids, w, s, topk_weights=tw)
+    assert_per_expert(got, ref, slot_experts(ids, E), "stream-K random")
+
+
+def test_stream_k_with_nothing_routed(gpu):
+    E, T, topk, K, N = 6, 50, 2, 1024, 512
+    rng = np.random.default_rng(430)
+    w, s = weights(rng, E, N, K)
+    a = inputs.bf16_normal(rng, (T, K))
+    ids = np.full((T, topk), -1, np.int32)
+    got, plan = indexed(a, topk, ids, w, s, force_bm=16,
+                        override={"block_n": 128, "waves_k": 1, "split_k": 1, "n_stream": 1,
+                                  "schedule": qma.SCHEDULE_STREAM_K})
+    assert plan.schedule == qma.SCHEDULE_STREAM_K
+    assert np.all(got == SENT)
+
+
 # Few token tiles are folded into column-block groups dealt to the XCDs
 # separately (the fold follows the plan's tile estimate, est_tiles / column
 # blocks). Folding moves work between workgroups only: every fold gives the
@@ -1049,6 +1124,8 @@ def test_randomized_plan_variants_bitwise(gpu, case):
         variants += [{"est_tiles": nb}, {"est_tiles": 3 * nb}, {"split_k": 2, "n_stream": 1}]
         if base.waves_k == 1 and base.n_stream == 1 and base.block_n in (128, 256) and bm <= 32:
             variants.append({"schedule": qma.SCHEDULE_GANG})
+            if K >= 1024:
+                variants.append({"schedule": qma.SCHEDULE_STREAM_K})
     for ov in variants:
         for W, want, cols in ((plain, ref, N), (fused, h_ref, N // 2)):
             plan = qma.qma_plan_indexed(W.layer, T, topk, bm)

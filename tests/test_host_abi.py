@@ -249,6 +249,59 @@ def test_gang_schedule_plan_rules():
     assert qma.qma_workspace_bytes(m) == 0
 
 
+def test_stream_k_schedule_rules():
+    from quantized_moe_align_amd import moe as moe_mod
+    fake = 1 << 20                                        # never dereferenced
+    lay = qma.qma_layer_create(48, 7168, 2048)
+    try:
+        p = qma.qma_plan_indexed(lay, 280, 2, 16)
+        assert p.block_m == 16 and p.waves_k == 1 and p.split_k == 1
+        p.schedule = qma.SCHEDULE_STREAM_K
+        assert qma.qma_workspace_bytes(p) == 0
+        assert moe_mod.schedule_applies(p, qma.SCHEDULE_STREAM_K)
+        bad = []
+        for field, value in (("split_k", 2), ("block_m", 64), ("waves_k", 4), ("n_stream", 2)):
+            q = qma.qma_plan_indexed(lay, 280, 2, 16)
+            setattr(q, field, value)
+            if field == "waves_k":
+                q.block_n = 64
+            q.schedule = qma.SCHEDULE_STREAM_K
+            assert not moe_mod.schedule_applies(q, qma.SCHEDULE_STREAM_K), field
+            with pytest.raises(qma.QmaError) as ei:
+                qma.qma_indexed_gemm(lay, q, fake, 280, 2, fake, fake, fake, fake,
+                                     560 + 48 * 63, 560, None, fake, stream=0)
+            bad.append(ei.value.status == qma.QMA_ERR_INVALID_ARG)
+        assert all(bad)
+        # a sorted capacity that could give a group items of three token tiles
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_indexed_gemm(lay, p, fake, 280, 2, fake, fake, fake, fake, 1 << 16, 560,
+                                 None, fake, stream=0)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG and "stream-K" in str(ei.value)
+    finally:
+        qma.qma_layer_destroy(lay)
+    # indexed layers only; short K (fewer than 8 chunks) refused
+    m = qma.qma_layer_create(48, 7168, 2048, qma.PATH_GROUPED_MASKED)
+    try:
+        q = qma.qma_plan_grouped(m, 64, 32)
+        q.schedule = qma.SCHEDULE_STREAM_K
+        assert not moe_mod.schedule_applies(q, qma.SCHEDULE_STREAM_K)
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_grouped_masked_gemm(m, q, fake, fake, 64, 32, fake, fake, stream=0)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG
+    finally:
+        qma.qma_layer_destroy(m)
+    short = qma.qma_layer_create(8, 7168, 512)
+    try:
+        q = qma.qma_plan_indexed(short, 64, 2, 16)
+        q.schedule, q.n_stream, q.block_n = qma.SCHEDULE_STREAM_K, 1, 128
+        with pytest.raises(qma.QmaError) as ei:
+            qma.qma_indexed_gemm(short, q, fake, 64, 2, fake, fake, fake, fake, 128 + 8 * 15,
+                                 128, None, fake, stream=0)
+        assert ei.value.status == qma.QMA_ERR_INVALID_ARG
+    finally:
+        qma.qma_layer_destroy(short)
+
+
 def test_dynamic_schedule_plan_rules():
     p = _plan(48, 4096, 7168, 576, 1)
     p.schedule = qma.SCHEDULE_SEMI_STATIC

@@ -6,7 +6,8 @@ an edited plan can launch must run without scratch: a spilled VGPR turns
 into a private-memory round trip inside the K loop. The shared-row small-M
 instances must also fit the workgroups per compute unit they are built for
 (four: at most 128 VGPRs and a quarter of the LDS; three for the 32-row,
-4-tile instance), and the gang instances one workgroup of three groups.
+4-tile instance), the gang instances one workgroup of three groups, and the
+stream-K instances one workgroup of four (three at 256 columns) groups.
 """
 import os
 import re
@@ -51,7 +52,7 @@ def resources(tmp_path_factory):
 def test_every_kernel_reports(resources):
     names = " ".join(resources)
     for k in ("gemm_small_m_xs_kernel", "gemm_small_m_xs_dyn_kernel",
-              "gemm_small_m_xs_gang_kernel", "gemm_small_m_kernel",
+              "gemm_small_m_xs_gang_kernel", "gemm_small_m_sk_kernel", "gemm_small_m_kernel",
               "gemm_small_m_stream_kernel", "gemm_large_m_kernel", "gemm_large_m_pc_kernel",
               "splitk_reduce_kernel", "moe_align_kernel"):
         assert k in names, k
@@ -84,3 +85,15 @@ def test_gang_instances_fit_one_workgroup_per_cu(resources):
     for n, r in gang.items():
         assert r["VGPRs"] <= 512 // 3 // 8 * 8, (n, r["VGPRs"])
         assert r["LDS Size"] <= 160 * 1024, (n, r["LDS Size"])
+
+
+def test_stream_k_instances_fit_one_workgroup_per_cu(resources):
+    # four four-wave groups for the 128-column instances (at most 128 VGPRs),
+    # three for the 256-column ones; the groups' LDS within one CU's 160 KiB
+    sk = {n: r for n, r in resources.items() if "gemm_small_m_sk_kernel" in n}
+    assert len(sk) == 4, sorted(sk)
+    for n, r in sk.items():
+        groups = 3 if "Li4ELi3EE" in n else 4
+        assert r["VGPRs"] <= 512 // groups // 8 * 8, (n, r["VGPRs"])
+        assert r["LDS Size"] <= 160 * 1024, (n, r["LDS Size"])
+
