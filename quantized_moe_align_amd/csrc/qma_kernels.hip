@@ -842,10 +842,6 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
   }
 }
 
-// Split-K reduction: c[row] = bf16( sum_s ws[s][row] (* topk weight) ), the
-// splits summed in order ([release] indexed techniques: the split/reduce
-// that the stream-K gate avoids on saturated grids). One thread per
-// (row position, 4 columns).
 // Streaming small-M variant for short K: one 16-token tile, one K
 // partition, the four waves side by side over 16 * NTW columns each. A
 // workgroup walks p.nstream consecutive column blocks of its expert: the
@@ -853,9 +849,15 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_kernel(const GemmParams p
 // pipeline, so the next block's weights are in flight while the current
 // block finishes, and a block's outputs are stored as soon as its last
 // chunk is accumulated. Token rows, output rows and topk weights are looked
-// up once per workgroup.
-template <int NTW, int D>
-__global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmParams p) {
+// up once per workgroup. With XR (K of one or two chunks) the token rows
+// are loaded once and stay in registers; the stages then hold weights
+// only, and two of them leave room for three workgroups per CU (TP8 down
+// share: 89.1-89.4 -> 81.9-82.2 us against four stages with the rows in
+// every stage; 83.1-83.8 us with resident rows and four stages at two
+// workgroups per CU).
+template <int NTW, int D, bool XR>
+__global__ __launch_bounds__(256, XR ? 3 : 2) void gemm_small_m_stream_kernel(const GemmParams p) {
+  static_assert(!XR || D % 2 == 0, "resident token rows: stage d holds chunk d % 2");
   int tile, grp, sp;
   if (!decode_bid(p, blockIdx.x, tile, grp, sp)) return;
   const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
@@ -892,9 +894,22 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
   struct Stage {
     u32x4 w[NTW];
     u32x2 s[NTW];
-    u32x4 x[4];
+    u32x4 x[XR ? 1 : 4];
   };
   Stage st[D];
+  // K of one or two chunks (XR): the tile's token rows for both chunks stay
+  // in registers for the whole stream instead of riding in every stage;
+  // the stream starts on chunk 0 and D is even, so stage d always holds
+  // chunk d % 2 (a one-chunk K loads chunk 0 twice).
+  u32x4 xres[XR ? 2 : 1][4];
+  if constexpr (XR) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        xres[c][g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64,
+                                                           min(c, KC - 1) * 256, 0);
+  }
   // load cursor: column block and chunk of the next stage to fetch
   int l_nb = nb0, l_c = 0;
   auto load_next = [&](Stage& s) {
@@ -909,9 +924,11 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
     for (int nt = 0; nt < NTW; ++nt)
       s.s[nt] = __builtin_amdgcn_raw_buffer_load_b64(rs, voff_s,
                                                      sa.base + nt * sa.tile + l_c * sa.chunk, 0);
+    if constexpr (!XR) {
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
+      for (int g = 0; g < 4; ++g)
+        s.x[g] = __builtin_amdgcn_raw_buffer_load_b128(ra, voff_x + g * 64, l_c * 256, 0);
+    }
     if (++l_c == KC) {
       l_c = 0;
       ++l_nb;
@@ -926,7 +943,12 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 
   // compute cursor: column block and chunk of the next stage to consume
   int c_nb = nb0, c_c = 0;
-  auto step = [&](const Stage& s) {
+  auto step = [&](const Stage& s, int d) {
+    const u32x4* sx;
+    if constexpr (XR)
+      sx = xres[d & 1];
+    else
+      sx = s.x;
     if constexpr (NTW == 4) {
       // The four zero-point MFMAs go first and products run one (group,
       // column tile) pair ahead of their scale FMAs, so no MFMA result is
@@ -935,7 +957,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
       // column tiles the extra registers would cost a workgroup per CU.)
       f32x4 xs[4];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) xs[g] = mfma16(s.x[g], neg136, zero4);
+      for (int g = 0; g < 4; ++g) xs[g] = mfma16(sx[g], neg136, zero4);
       f32x4 pr[2];
       float scv[2];
       auto product = [&](int i) {
@@ -943,7 +965,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
         const u32x4 wb = unpack_128q(s.w[nt][g]);
         const uint32_t sw = s.s[nt][g >> 1];
         scv[i & 1] = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-        pr[i & 1] = mfma16(s.x[g], wb, xs[g]);
+        pr[i & 1] = mfma16(sx[g], wb, xs[g]);
       };
       auto scale = [&](int i) {
         const int nt = i % NTW;
@@ -961,13 +983,13 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
     } else {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 xs = mfma16(s.x[g], neg136, zero4);
+        const f32x4 xs = mfma16(sx[g], neg136, zero4);
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt) {
           const u32x4 wb = unpack_128q(s.w[nt][g]);
           const uint32_t sw = s.s[nt][g >> 1];
           const float scv = (g & 1) ? bf16_hi(sw) : bf16_lo(sw);
-          const f32x4 pr = mfma16(s.x[g], wb, xs);
+          const f32x4 pr = mfma16(sx[g], wb, xs);
 #pragma unroll
           for (int r = 0; r < 4; ++r) acc[nt][r] = __builtin_fmaf(scv, pr[r], acc[nt][r]);
         }
@@ -1017,7 +1039,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         __builtin_amdgcn_sched_barrier(0);
-        step(st[d]);
+        step(st[d], d);
         __builtin_amdgcn_sched_barrier(0);
         load_next(st[d]);
       }
@@ -1032,7 +1054,7 @@ __global__ __launch_bounds__(256, 2) void gemm_small_m_stream_kernel(const GemmP
 #pragma unroll
     for (int d = 0; d < D; ++d) {
       if (f + d < total) {
-        step(st[d]);
+        step(st[d], d);
         if (f + d + D < total) load_next(st[d]);
       }
     }
@@ -1763,6 +1785,10 @@ int scratch_device_ptr(void** out) {
   return 0;
 }
 
+// Split-K reduction: c[row] = bf16( sum_s ws[s][row] (* topk weight) ), the
+// splits summed in order ([release] indexed techniques: the split/reduce
+// that the stream-K gate avoids on saturated grids). One thread per
+// (row position, 4 columns).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmParams p) {
   if (p.act) {
     // fused activation: four outputs h[row, o0 .. o0+3] per thread, from
@@ -2847,10 +2873,14 @@ int launch_gemm(const GemmArgs& g, void* stream) {
         hipLaunchKernelGGL((gemm_small_m_xs_kernel<2, 2, 2>), sg, dim3(256), 0, st, gp);
       else if (xs)
         hipLaunchKernelGGL((gemm_small_m_xs_kernel<4, 2, 2>), sg, dim3(256), 0, st, gp);
+      else if (ntw == 4 && gp.KC <= 2)
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 2, true>), sg, dim3(256), 0, st, gp);
       else if (ntw == 4)
-        hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4>), sg, dim3(256), 0, st, gp);
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<4, 4, false>), sg, dim3(256), 0, st, gp);
+      else if (gp.KC <= 2)
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 2, true>), sg, dim3(256), 0, st, gp);
       else
-        hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4>), sg, dim3(256), 0, st, gp);
+        hipLaunchKernelGGL((gemm_small_m_stream_kernel<2, 4, false>), sg, dim3(256), 0, st, gp);
       err = (int)hipGetLastError();
     }
   } else {
