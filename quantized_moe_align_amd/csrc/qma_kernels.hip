@@ -394,9 +394,11 @@ __device__ __forceinline__ int tile_expert(const GemmParams& p, int tile) {
 }
 
 // Row r of a tile: whether it holds a token, its activation row and its
-// output row.
+// output row. A tile without an expert (e < 0) holds none, and nothing is
+// read for it: a masked layer would otherwise index masked_m[-1].
 __device__ __forceinline__ RowInfo row_info(const GemmParams& p, int tile, int e, int r) {
   RowInfo ri{false, 0, 0};
+  if (e < 0) return ri;
   if (p.mode == 0) {
     const int pos = tile * p.BM + r;
     const int s = (pos < p.cap) ? p.sorted_ids[pos] : -1;
