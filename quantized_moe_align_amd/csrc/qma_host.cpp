@@ -9,7 +9,8 @@
 //     the indexed kernels accept over-allocated routing buffers and are
 //     graph-capturable when routing validation is off.
 //   [release] indexed techniques: the tok_e block-M rule with threshold 80;
-//     the stream-K (here split-K) gate.
+//     the stream-K gate (here split-K; a stream-K schedule that cuts items
+//     in K inside a CU's share is accepted from edited plans).
 //   [release] grouped techniques: BN256 only with enough N tiles (here the
 //     wider of two workgroup widths); BLOCK_M from the expected token
 //     count; a buffered K depth of about 512, up to about 768 for large

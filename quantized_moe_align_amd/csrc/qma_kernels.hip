@@ -1460,7 +1460,7 @@ __global__ __launch_bounds__(256 * S, 1) void gemm_small_m_xs_gang_kernel(const 
 // the launch as a semi-static grid's last round leaves it. A group walks
 // its chunks as one stream through the shared-row pipeline: the next
 // item's loads are in flight while the current one finishes. A finished
-// item is packed to bf16 at once and stored at the next step, ahead of
+// item stays in the accumulators and is stored at the next step, ahead of
 // that step's loads, so the pipeline's wait counts never include stores.
 // An item cut in K: the group holding its first chunk (the owner) keeps
 // its piece in registers to the end; a group whose range starts inside
