@@ -690,8 +690,7 @@ qma_status qma_indexed_gemm(const qma_layer_t* layer, const qma_plan_t* plan,
     return s;
   if (plan->schedule == QMA_SCHEDULE_STREAM_K &&
       !qma::stream_k_fits(((int64_t)sorted_cap + plan->block_m - 1) / plan->block_m,
-                          layer->L.N / plan->block_n, layer->L.k_chunks, plan->block_m / 16,
-                          plan->block_n / 64))
+                          layer->L.N / plan->block_n, layer->L.k_chunks, plan->block_n / 64))
     return fail(QMA_ERR_INVALID_ARG,
                 "stream-K: sorted_cap %d gives a group items of more than two token tiles "
                 "(%d column blocks per tile)", sorted_cap, layer->L.N / plan->block_n);

@@ -128,14 +128,14 @@ int launch_gemm(const GemmArgs& g, void* stream);
 
 // Groups per stream-K workgroup: four for the 128-column instances (at
 // most 128 VGPRs), three for the 256-column ones (at most 168).
-constexpr int sk_groups(int tm, int ntw) { return ntw == 4 ? 3 : 4; }
+constexpr int sk_groups(int ntw) { return ntw == 4 ? 3 : 4; }
 
 // Whether a stream-K launch keeps every group's unit range within two token
 // tiles for any routed tile count up to num_tiles: a workgroup holds at
 // most ceil(items / CUs) items, a group ceil(that * KC / S) units, and a
 // range of L units touches at most 1 + ceil((L - 1) / KC) items.
-inline bool stream_k_fits(int64_t num_tiles, int64_t nblocks, int64_t kc, int tm, int ntw) {
-  const int S = sk_groups(tm, ntw);
+inline bool stream_k_fits(int64_t num_tiles, int64_t nblocks, int64_t kc, int ntw) {
+  const int S = sk_groups(ntw);
   if (num_tiles <= 0 || nblocks <= 0 || kc <= 0) return false;
   const int64_t per_wg = (num_tiles * nblocks + kNumCUs - 1) / kNumCUs;
   if (per_wg * kc >= (1ll << 30)) return false;

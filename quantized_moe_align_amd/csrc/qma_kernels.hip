@@ -2841,17 +2841,17 @@ int launch_gemm(const GemmArgs& g, void* stream) {
     const dim3 sg((unsigned)(vt_pad * (gp.nblocks / gp.fold) * gp.split));
     if (pl.schedule == QMA_SCHEDULE_STREAM_K) {
       if (!xs || g.mode != 0 || gp.split != 1 || tm > 2 || gp.KC < kStreamChunks ||
-          gp.nstream != 1 || !stream_k_fits(g.num_tiles, gp.nblocks, gp.KC, tm, ntw))
+          gp.nstream != 1 || !stream_k_fits(g.num_tiles, gp.nblocks, gp.KC, ntw))
         return (int)hipErrorInvalidConfiguration;
       gp.fold = 1;
       if (tm == 1 && ntw == 4)
-        err = launch_sk<1, 4, sk_groups(1, 4)>(gp, st);
+        err = launch_sk<1, 4, sk_groups(4)>(gp, st);
       else if (tm == 1)
-        err = launch_sk<1, 2, sk_groups(1, 2)>(gp, st);
+        err = launch_sk<1, 2, sk_groups(2)>(gp, st);
       else if (ntw == 4)
-        err = launch_sk<2, 4, sk_groups(2, 4)>(gp, st);
+        err = launch_sk<2, 4, sk_groups(4)>(gp, st);
       else
-        err = launch_sk<2, 2, sk_groups(2, 2)>(gp, st);
+        err = launch_sk<2, 2, sk_groups(2)>(gp, st);
     } else if (pl.schedule == QMA_SCHEDULE_GANG) {
       if (!xs) return (int)hipErrorInvalidConfiguration;
       if (tm == 1 && ntw == 4)
