@@ -374,12 +374,15 @@ struct RowInfo {
   int32_t out_row;
 };
 
-// The tile's expert, or -1 for a tile with no work.
+// The tile's expert, or -1 for a tile with no work. (tile < num_tiles, so
+// expert_ids[tile] lies inside the buffer even past the routed blocks; it is
+// read beside num_tokens_padded rather than after it, one memory round trip
+// instead of two.)
 __device__ __forceinline__ int tile_expert(const GemmParams& p, int tile) {
   if (p.mode == 0) {
-    if (tile * p.BM >= *p.ntp) return -1;
+    const int ntp = *p.ntp;
     const int e = p.expert_ids[tile];
-    return (e >= 0 && e < p.E) ? e : -1;
+    return (tile * p.BM < ntp && e >= 0 && e < p.E) ? e : -1;
   }
   if (p.mode == 1) {
     const int e = p.m_indices[tile * p.BM];
@@ -1218,12 +1221,37 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   constexpr int NX = TM;                     // direct-to-LDS loads per wave and chunk
   constexpr int NW = 2 * NTW;                // weight + scale loads per wave and chunk
   static_assert(D >= 2, "pipeline depth");
-  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
-  if (e < 0) return;
-
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 15, kb = lane >> 4;
+  // Indexed routing: the slots of the rows this lane will look up are read
+  // together with the tile's expert, so that the first token-row loads wait
+  // one memory round trip rather than two.
+  int sid_x[NX], sid_t = -1;
+  if (p.mode == 0) {
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int pos = tile * p.BM + 4 * (w * NX + i) + kb;
+      sid_x[i] = pos < p.cap ? p.sorted_ids[pos] : -1;
+    }
+    if (w == 0 && lane < TM * 16) {
+      const int pos = tile * p.BM + lane;
+      sid_t = pos < p.cap ? p.sorted_ids[pos] : -1;
+    }
+  }
+  const int e = __builtin_amdgcn_readfirstlane(tile_expert(p, tile));
+  if (e < 0) return;
+  // row_info from a slot read above (indexed routing), else looked up
+  auto row_of = [&](int sid, int row) __attribute__((always_inline)) {
+    if (p.mode != 0) return row_info(p, tile, e, row);
+    RowInfo ri{false, 0, 0};
+    if (sid >= 0 && sid < p.num_slots) {
+      ri.valid = true;
+      ri.a_row = sid / p.a_row_div;
+      ri.out_row = sid;
+    }
+    return ri;
+  };
   const int KC = p.KC;
   // this workgroup's K range (all of K without split-K; the host keeps
   // split_k <= K / 128, so every range holds a chunk)
@@ -1249,7 +1277,7 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
 #pragma unroll
   for (int i = 0; i < NX; ++i) {
     const int row = 4 * (w * NX + i) + kb;
-    const RowInfo ri = row_info(p, tile, e, row);
+    const RowInfo ri = row_of(sid_x[i], row);
     const uint32_t seg = (uint32_t)(col ^ (row & 15));
     voff_x[i] = ri.valid ? (uint32_t)ri.a_row * (uint32_t)p.K * 2u + seg * 16u : 0x80000000u;
   }
@@ -1262,7 +1290,7 @@ __device__ __forceinline__ void xs_tile(const GemmParams& p, int tile, int nb, i
   int32_t my_orow = -1;
   float my_tw = 1.0f;
   if (w == 0 && lane < TM * 16) {
-    const RowInfo ri = row_info(p, tile, e, lane);
+    const RowInfo ri = row_of(sid_t, lane);
     my_orow = ri.valid ? ri.out_row : -1;
     my_tw = (ri.valid && scale_rows) ? p.topk_w[ri.out_row] : 1.0f;
   }
