@@ -531,3 +531,53 @@ def test_planner_invariants_over_shapes():
             assert qma.qma_workspace_bytes(p) > 0, shape
         else:
             assert qma.qma_workspace_bytes(p) == 0, shape
+
+
+def _sk_fits(num_tiles, nblocks, kc, groups, cus=256):
+    # the host's bound for the stream-K schedule (a group's range of units
+    # touches at most two token tiles), written out from its definition
+    per_wg = -(-(num_tiles * nblocks) // cus)
+    per_group = -(-(per_wg * kc) // groups)
+    span = 1 + -(-(per_group - 1) // kc)
+    return span - 1 <= nblocks
+
+
+def test_stream_k_work_division_model():
+    """The stream-K schedule's work division, walked unit by unit as each
+    group of a CU walks it: every K chunk of every item is accumulated once,
+    the pieces of an item cut between groups meet at the group holding its
+    first chunk in K order, and no group meets a third token tile whenever
+    the host's bound admits the shape. Brute force over random shapes."""
+    import random
+    rng = random.Random(7)
+    cases = [(48, 56, 16, 4), (3, 56, 16, 4), (1, 1, 8, 4), (5, 2, 8, 3), (384, 56, 2, 4)]
+    cases += [(rng.randint(1, 300), rng.randint(1, 60), rng.randint(8, 56), rng.choice([3, 4]))
+              for _ in range(150)]
+    checked = 0
+    for ntiles, nbl, kc, S in cases:
+        if not _sk_fits(ntiles, nbl, kc, S):
+            continue
+        checked += 1
+        items, grid = ntiles * nbl, 256
+        pieces = {}
+        for b in range(grid):
+            rk = (b & 7) * (grid >> 3) + (b >> 3)
+            i0, i1 = items * rk // grid, items * (rk + 1) // grid
+            if i0 >= i1:
+                continue
+            U = (i1 - i0) * kc
+            starts = [U * k // S for k in range(S + 1)]
+            for g in range(S):
+                ua, ub = starts[g], starts[g + 1]
+                assert ub - ua >= 2
+                tiles = {(i0 + u // kc) // nbl for u in range(ua, ub)}
+                assert max(tiles) - min(tiles) <= 1, (ntiles, nbl, kc, S, b, g)
+                for u in range(ua, ub):
+                    pieces.setdefault(i0 + u // kc, []).append((g, u % kc))
+        assert sorted(pieces) == list(range(items))
+        for item, units in pieces.items():
+            # every chunk once, the groups in ascending order along K
+            assert [c for _, c in units] == list(range(kc)), item
+            gs = [g for g, _ in units]
+            assert gs == sorted(gs), item
+    assert checked > 100
